@@ -1,0 +1,202 @@
+/*
+ * moe_mi355x.h -- C ABI of the sparse MoE FFN block for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The block (Qwen3-style sparse MoE FFN) is defined on the page "M03 · Sparse
+ * MoE：路由、按 expert 分组计算、shared expert", section 题面速览:
+ *
+ *   logits = x . router_w^T                       [N, E]
+ *   probs  = softmax over all E experts, float32
+ *   (w, ids) = top-k of probs, descending
+ *   if norm_topk_prob: w /= sum_j w
+ *   out[n] = sum_j w[n,j] * Expert_{ids[n,j]}(x[n])
+ *            (+ sigmoid(x[n] . g) * Shared(x[n]) for the shared-expert variant)
+ *   Expert(h) = (silu(h Wg^T) * (h Wu^T)) Wd^T
+ *
+ * and computed "the serving way" of the same section: (token, slot) pairs
+ * grouped by expert with a stable sort, one grouped product per expert over
+ * its gathered tokens, and a weighted accumulation back to each token.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers (HBM of the current HIP device)
+ *   to dense row-major arrays; the caller owns and allocates every buffer.
+ *   The library keeps no device memory between calls.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on that stream and returns; nothing synchronises the host
+ *   and no buffer is read on the host, so calls can be captured in a graph.
+ * - Pair index: p = n*top_k + j for token n and slot j (token-major).
+ * - dtype: MOE_F32 -- x, every weight, out and the internal activations are
+ *   float32 (any shapes).  MOE_BF16 -- x, every weight and out are bfloat16,
+ *   all products accumulate in float32; requires hidden, inter and
+ *   shared_inter to be multiples of 64 and 16-byte aligned pointers.
+ * - Router logits, probabilities and routing weights are float32 in both
+ *   dtypes; expert ids are int32.
+ * - Return value: MOE_OK (0) or a negative MOE_E* code.  Arguments are fully
+ *   validated before any HIP call; on error nothing is enqueued and
+ *   moe_last_error() describes the problem.  num_tokens == 0 is valid and
+ *   enqueues nothing.
+ * - Limits: 1 <= top_k <= num_experts <= 512, top_k <= 32.
+ * - An entry point validates only the moe_problem fields it uses (moe_route:
+ *   tokens, hidden, experts, top_k, dtype, norm_topk_prob; moe_gate_up and
+ *   moe_down add inter; moe_shared_expert: tokens, hidden, top_k, dtype and
+ *   shared_inter; moe_combine: tokens, hidden, top_k, dtype).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* null pointer, bad shape, top_k outside [1, E] */
+  MOE_ENOSPC = -2,        /* workspace too small */
+  MOE_EUNSUPPORTED = -3,  /* dtype, alignment or size outside the limits */
+  MOE_EHIP = -4           /* a HIP launch failed */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Shape and options of one MoE layer call. */
+typedef struct moe_problem {
+  int64_t num_tokens;      /* N  */
+  int64_t hidden;          /* H  */
+  int64_t num_experts;     /* E  */
+  int64_t top_k;           /* k  */
+  int64_t inter;           /* I  : expert intermediate size */
+  int64_t shared_inter;    /* I_s: shared-expert intermediate size, 0 = none */
+  int32_t dtype;           /* MOE_F32 or MOE_BF16 */
+  int32_t norm_topk_prob;  /* 1: renormalise the k kept weights to sum 1 */
+} moe_problem;
+
+/* Byte offsets of the regions moe_forward carves out of its workspace, and
+ * the tile height (block_m) it groups with.  Offsets are 256-byte aligned;
+ * a region of size 0 has offset equal to the previous end. */
+typedef struct moe_workspace_layout {
+  int64_t block_m;         /* rows per grouped-GEMM tile */
+  int64_t max_rows;        /* capacity of sorted_pairs / act rows */
+  int64_t max_tiles;       /* capacity of tile_expert / tile_rows */
+  size_t topk_ids, topk_w, shared_scale;
+  size_t counts, offsets, order, sorted_pairs, tile_expert, tile_rows, num_tiles;
+  size_t act, y, shared_act, shared_y;
+  size_t total_bytes;
+} moe_workspace_layout;
+
+/* Workspace moe_forward needs for `p` (bytes) and where each region lies.
+ * Pure host arithmetic; never touches the GPU. */
+int moe_workspace_size(const moe_problem* p, size_t* bytes);
+int moe_get_workspace_layout(const moe_problem* p, moe_workspace_layout* layout);
+
+/* Capacity of the padded grouping for num_pairs pairs over num_experts
+ * experts with tile height block_m: max_rows = max_tiles * block_m, where
+ * max_tiles = (num_pairs + min(E, num_pairs) * (block_m - 1)) / block_m.
+ * Pure host arithmetic. */
+int moe_align_capacity(int64_t num_pairs, int64_t num_experts, int64_t block_m,
+                       int64_t* max_rows, int64_t* max_tiles);
+
+/* Router (M03 题面速览, routing block; "Nano-vLLM 代码笔记 (八)",
+ * Qwen3MoeSparseMoeBlock forward).
+ *   x          [N, H]  dtype
+ *   router_w   [E, H]  dtype
+ *   shared_gate [H]    dtype or NULL; if given, shared_scale[n] =
+ *                      sigmoid(x[n] . shared_gate) is written (float32 [N])
+ *   topk_ids   [N, k]  int32 out: experts by descending probability, equal
+ *                      probabilities to the lower expert id
+ *   topk_w     [N, k]  float32 out: the probabilities of those experts,
+ *                      divided by their sum when norm_topk_prob is set
+ * Logits are accumulated in float32; softmax runs over all E in float32. */
+int moe_route(const moe_problem* p, const void* x, const void* router_w,
+              const void* shared_gate, int32_t* topk_ids, float* topk_w,
+              float* shared_scale, void* stream);
+
+/* Grouping of the N*k pairs by expert (M03 逐步图 steps 1-3: flatten, stable
+ * sort by expert id, per-expert counts and segment starts; the padding to
+ * the tile height is what the pages call aligning to a block).
+ *   topk_ids     [N*k]       int32 in, each in [0, E)
+ *   counts       [E]         int32 out: pairs per expert
+ *   offsets      [E+1]       int32 out: exclusive prefix sum of counts
+ *   order        [N*k]       int32 out: pair indices sorted by expert id,
+ *                            ascending pair index within an expert (stable)
+ *   sorted_pairs [max_rows]  int32 out: each expert's segment of `order`
+ *                            padded with the sentinel N*k to a multiple of
+ *                            block_m, experts ascending, empty ones skipped;
+ *                            entries past the last tile are not written
+ *   tile_expert  [max_tiles] int32 out: expert of tile t (rows
+ *                            [t*block_m, (t+1)*block_m) of sorted_pairs)
+ *   tile_rows    [max_tiles] int32 out: real (non-sentinel) rows of tile t
+ *   num_tiles    [1]         int32 out: number of tiles written
+ * Capacities come from moe_align_capacity.  block_m in [1, 1024]. */
+int moe_align(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k,
+              int64_t num_experts, int64_t block_m, int32_t* counts,
+              int32_t* offsets, int32_t* order, int32_t* sorted_pairs,
+              int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles,
+              void* stream);
+
+/* Grouped gate/up product with the SwiGLU epilogue (M03 题面速览 expert
+ * formula; L1 细节 weight shapes): for every tile row r holding pair p,
+ *   act[r, i] = silu(x[p / k] . Wg[e, i]) * (x[p / k] . Wu[e, i]),
+ * with w_gate_up[e] = [Wg[e] (rows 0..I-1); Wu[e] (rows I..2I-1)].
+ *   w_gate_up [E, 2I, H] dtype;  act [max_rows, I] dtype out (sentinel rows
+ *   are left unwritten).  Grouping arrays as produced by moe_align with the
+ *   same block_m; max_tiles bounds the launch, *num_tiles is read on the
+ *   device. */
+int moe_gate_up(const moe_problem* p, const void* x, const void* w_gate_up,
+                const int32_t* sorted_pairs, const int32_t* tile_expert,
+                const int32_t* tile_rows, const int32_t* num_tiles,
+                int64_t block_m, int64_t max_tiles, void* act, void* stream);
+
+/* Grouped down product with the routing-weight epilogue (M03 题面速览;
+ * "Nano-vLLM 代码笔记 (八)", the expert output times its routing weight):
+ * for every tile row r holding pair p,
+ *   y[p, h] = topk_w[p] * (act[r] . Wd[e, h]),
+ *   w_down [E, H, I] dtype;  topk_w [N*k] float32;  y [N*k, H] dtype out,
+ *   every row written once. */
+int moe_down(const moe_problem* p, const void* act, const void* w_down,
+             const float* topk_w, const int32_t* sorted_pairs,
+             const int32_t* tile_expert, const int32_t* tile_rows,
+             const int32_t* num_tiles, int64_t block_m, int64_t max_tiles,
+             void* y, void* stream);
+
+/* Shared expert (M03 题面速览, talker's shared expert; "Qwen3.5 推理全流程"
+ * 2.5B formula, second term): dense over all N tokens,
+ *   shared_act[n] = silu(x[n] Wg_s^T) * (x[n] Wu_s^T)        [N, I_s]
+ *   shared_y[n]   = shared_scale[n] * (shared_act[n] Wd_s^T)  [N, H]
+ *   shared_w_gate_up [2 I_s, H], shared_w_down [H, I_s], dtype. */
+int moe_shared_expert(const moe_problem* p, const void* x,
+                      const void* shared_w_gate_up, const void* shared_w_down,
+                      const float* shared_scale, void* shared_act,
+                      void* shared_y, void* stream);
+
+/* Deterministic combine (M03 逐步图 step 4 and 易错点: contributions of a
+ * token's slots are added, never assigned):
+ *   out[n] = sum_{j = 0..k-1} y[n*k + j]  (+ shared_y[n] if non-NULL),
+ * summed in float32 in that fixed order and rounded once to dtype.
+ * out [N, H] dtype is fully overwritten. */
+int moe_combine(const moe_problem* p, const void* y, const void* shared_y,
+                void* out, void* stream);
+
+/* The whole block: moe_route, moe_align, moe_gate_up, moe_down,
+ * [moe_shared_expert], moe_combine on one stream, in that order, with every
+ * intermediate in `workspace` (moe_workspace_size bytes, 256-byte aligned,
+ * laid out as moe_get_workspace_layout says).  shared_w_gate_up == NULL means
+ * no shared expert (then shared_w_down and shared_gate are ignored and
+ * p->shared_inter must be 0). */
+int moe_forward(const moe_problem* p, const void* x, const void* router_w,
+                const void* w_gate_up, const void* w_down,
+                const void* shared_w_gate_up, const void* shared_w_down,
+                const void* shared_gate, void* out, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -65,44 +65,35 @@ def router_logits(x, router_w) -> np.ndarray:
     return (x64 @ r64.T).astype(F32)
 
 
-def softmax_f32(logits_row: np.ndarray) -> np.ndarray:
-    """Float32 softmax over all experts of one token: exp(l - max) / sum."""
-    l = np.asarray(logits_row, dtype=F32)
-    m = F32(l.max())
+def softmax_f32(logits) -> np.ndarray:
+    """Float32 softmax over all experts (last axis): exp(l - max) / sum, the
+    sum taken sequentially in expert order in float32."""
+    l = np.asarray(logits, dtype=F32)
+    m = l.max(axis=-1, keepdims=True)
     z = np.exp(l - m).astype(F32)
-    s = F32(0.0)
-    for v in z:                     # sequential float32 sum in expert order
-        s = F32(s + v)
+    s = np.add.accumulate(z, axis=-1, dtype=F32)[..., -1:]
     return (z / s).astype(F32)
 
 
-def topk_desc(values: np.ndarray, k: int):
-    """k passes of argmax: descending values, equal values to the lower index."""
-    v = [float(t) for t in values]
-    taken = [False] * len(v)
-    ids, vals = [], []
-    for _ in range(k):
-        best = -1
-        for e in range(len(v)):
-            if taken[e]:
-                continue
-            if best < 0 or v[e] > v[best]:      # strict '>' keeps the lower id on ties
-                best = e
-        taken[best] = True
-        ids.append(best)
-        vals.append(values[best])
-    return np.array(ids, dtype=np.int64), np.array(vals, dtype=F32)
+def topk_desc(values, k: int):
+    """The k largest values along the last axis, in descending order; equal
+    values keep ascending index order (a stable sort of the negated values)."""
+    v = np.asarray(values, dtype=F32)
+    ids = np.argsort(-v, axis=-1, kind="stable")[..., :k].astype(np.int64)
+    return ids, np.take_along_axis(v, ids, axis=-1)
 
 
-def topk_margin(probs_row: np.ndarray, k: int) -> float:
-    """Smallest gap between adjacent values of the sorted probabilities at
-    ranks 0..k (the k-th/(k+1)-th gap included when k < E).  A token whose
-    margin is tiny can be routed either way by float32 rounding."""
-    s = np.sort(np.asarray(probs_row, dtype=F64))[::-1]
-    last = min(k + 1, s.shape[0])
+def topk_margin(probs, k: int):
+    """Smallest gap between adjacent values of the descending probabilities at
+    ranks 0..k (the k-th/(k+1)-th gap included when k < E); inf when E = 1.
+    A token whose margin is tiny can be routed either way by float32 rounding."""
+    p = np.asarray(probs, dtype=F64)
+    s = -np.sort(-p, axis=-1)
+    last = min(k + 1, p.shape[-1])
     if last < 2:
-        return math.inf
-    return float(np.min(s[: last - 1] - s[1:last]))
+        return np.full(p.shape[:-1], math.inf) if p.ndim > 1 else math.inf
+    gaps = np.min(s[..., : last - 1] - s[..., 1:last], axis=-1)
+    return gaps if p.ndim > 1 else float(gaps)
 
 
 def route(x, router_w, top_k: int, norm_topk_prob: bool):
@@ -114,22 +105,15 @@ def route(x, router_w, top_k: int, norm_topk_prob: bool):
     N, E = logits.shape
     if not (1 <= top_k <= E):
         raise ValueError("top_k must be in [1, E]")
-    ids = np.zeros((N, top_k), dtype=np.int64)
-    w = np.zeros((N, top_k), dtype=F32)
-    probs = np.zeros((N, E), dtype=F32)
-    margin = np.zeros(N, dtype=F64)
-    for n in range(N):
-        p = softmax_f32(logits[n])
-        probs[n] = p
-        i, v = topk_desc(p, top_k)
-        if norm_topk_prob:
-            s = F32(0.0)
-            for t in v:
-                s = F32(s + t)
-            v = (v / s).astype(F32)
-        ids[n], w[n] = i, v
-        margin[n] = topk_margin(p, top_k)
-    return ids, w, probs, margin
+    probs = softmax_f32(logits)
+    ids, w = topk_desc(probs, top_k)
+    if norm_topk_prob:
+        s = np.zeros((N, 1), dtype=F32)
+        for j in range(top_k):                    # sequential float32 sum in slot order
+            s = (s + w[:, j:j + 1]).astype(F32)
+        w = (w / s).astype(F32)
+    margin = topk_margin(probs, top_k) if N else np.zeros(0)
+    return ids, w.astype(F32), probs, np.asarray(margin, dtype=F64).reshape(N)
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,308 @@
+"""Python binding of the C ABI in ``include/moe_mi355x.h``.
+
+Argument marshalling only: every function checks that its tensors are
+contiguous, on one GPU and of the expected dtype, allocates missing outputs
+with torch (device memory is torch's), passes raw pointers and torch's current
+stream, and raises ``MoEError`` with the library's message on a non-zero
+return.  All computation happens in the HIP kernels of
+``libmoe_mi355x.so``; there is no fallback: if the library is missing, or
+has no GPU to run on, calls fail.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+
+_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"moe error {code}: {msg}")
+        self.code = code
+
+
+class MoEProblem(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("num_experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
+                ("inter", ctypes.c_int64), ("shared_inter", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32)]
+
+
+class MoEWorkspaceLayout(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int64), ("max_rows", ctypes.c_int64), ("max_tiles", ctypes.c_int64)] + [
+        (n, ctypes.c_size_t) for n in ("topk_ids", "topk_w", "shared_scale", "counts", "offsets", "order",
+                                       "sorted_pairs", "tile_expert", "tile_rows", "num_tiles", "act", "y",
+                                       "shared_act", "shared_y", "total_bytes")]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def load_library() -> ctypes.CDLL:
+    """The HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_moe_ffn_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        PP = ctypes.POINTER(MoEProblem)
+        sig = {
+            "moe_workspace_size": [PP, ctypes.POINTER(ctypes.c_size_t)],
+            "moe_get_workspace_layout": [PP, ctypes.POINTER(MoEWorkspaceLayout)],
+            "moe_align_capacity": [_I64, _I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
+            "moe_route": [PP, _P, _P, _P, _P, _P, _P, _P],
+            "moe_align": [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P],
+            "moe_gate_up": [PP, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P],
+            "moe_down": [PP, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P],
+            "moe_shared_expert": [PP, _P, _P, _P, _P, _P, _P, _P],
+            "moe_combine": [PP, _P, _P, _P, _P],
+            "moe_forward": [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+        }
+        for name, args in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        lib.moe_last_error.argtypes = []
+        lib.moe_last_error.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoEError(rc, load_library().moe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _gpu(t: torch.Tensor, name: str, dtype=None, device=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def problem(num_tokens, hidden, num_experts, top_k, inter, shared_inter=0, dtype=torch.bfloat16,
+            norm_topk_prob=True) -> MoEProblem:
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return MoEProblem(int(num_tokens), int(hidden), int(num_experts), int(top_k), int(inter),
+                      int(shared_inter), _DTYPES[dtype], int(bool(norm_topk_prob)))
+
+
+def problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up=None) -> MoEProblem:
+    N, H = x.shape
+    E, two_i, H2 = w_gate_up.shape
+    if H2 != H or two_i % 2 or router_w.shape != (E, H):
+        raise ValueError("shape mismatch between x, router_w and w_gate_up")
+    Is = 0 if shared_w_gate_up is None else shared_w_gate_up.shape[0] // 2
+    return problem(N, H, E, top_k, two_i // 2, Is, x.dtype, norm_topk_prob)
+
+
+def moe_workspace_size(p: MoEProblem) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().moe_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def moe_get_workspace_layout(p: MoEProblem) -> dict:
+    L = MoEWorkspaceLayout()
+    _check(load_library().moe_get_workspace_layout(ctypes.byref(p), ctypes.byref(L)))
+    return {name: getattr(L, name) for name, _ in MoEWorkspaceLayout._fields_}
+
+
+def moe_align_capacity(num_pairs: int, num_experts: int, block_m: int):
+    r, t = _I64(), _I64()
+    _check(load_library().moe_align_capacity(num_pairs, num_experts, block_m, ctypes.byref(r), ctypes.byref(t)))
+    return r.value, t.value
+
+
+def moe_route(x, router_w, top_k, norm_topk_prob, shared_gate=None, topk_ids=None, topk_w=None,
+              shared_scale=None):
+    """(topk_ids int32 [N,k], topk_w float32 [N,k], shared_scale float32 [N] or None)."""
+    x = _gpu(x, "x")
+    dev = x.device
+    router_w = _gpu(router_w, "router_w", x.dtype, dev)
+    N, H = x.shape
+    E = router_w.shape[0]
+    p = problem(N, H, E, top_k, 1, 0, x.dtype, norm_topk_prob)
+    if shared_gate is not None:
+        shared_gate = _gpu(shared_gate, "shared_gate", x.dtype, dev)
+        if shared_gate.numel() != H:
+            raise ValueError("shared_gate must have H elements")
+        if shared_scale is None:
+            shared_scale = torch.empty(N, dtype=torch.float32, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((N, top_k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((N, top_k), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_route(ctypes.byref(p), _ptr(x), _ptr(router_w), _ptr(shared_gate),
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(shared_scale), _stream(dev)))
+    return topk_ids, topk_w, shared_scale
+
+
+@dataclass
+class Grouping:
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    order: torch.Tensor
+    sorted_pairs: torch.Tensor
+    tile_expert: torch.Tensor
+    tile_rows: torch.Tensor
+    num_tiles: torch.Tensor
+    block_m: int
+    max_rows: int
+    max_tiles: int
+
+
+def moe_align(topk_ids, num_experts: int, block_m: int) -> Grouping:
+    topk_ids = _gpu(topk_ids, "topk_ids", torch.int32)
+    dev = topk_ids.device
+    N, k = topk_ids.shape
+    P = N * k
+    max_rows, max_tiles = moe_align_capacity(P, num_experts, block_m)
+    i32 = dict(dtype=torch.int32, device=dev)
+    g = Grouping(torch.empty(num_experts, **i32), torch.empty(num_experts + 1, **i32), torch.empty(P, **i32),
+                 torch.empty(max_rows, **i32), torch.empty(max_tiles, **i32), torch.empty(max_tiles, **i32),
+                 torch.empty(1, **i32), block_m, max_rows, max_tiles)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_align(_ptr(topk_ids), N, k, num_experts, block_m, _ptr(g.counts),
+                                        _ptr(g.offsets), _ptr(g.order), _ptr(g.sorted_pairs),
+                                        _ptr(g.tile_expert), _ptr(g.tile_rows), _ptr(g.num_tiles),
+                                        _stream(dev)))
+    return g
+
+
+def moe_gate_up(x, w_gate_up, grouping: Grouping, top_k: int, act=None):
+    """act [max_rows, I] in x.dtype (rows of sentinel pairs are not written)."""
+    x = _gpu(x, "x")
+    dev = x.device
+    w_gate_up = _gpu(w_gate_up, "w_gate_up", x.dtype, dev)
+    N, H = x.shape
+    E, two_i, _ = w_gate_up.shape
+    p = problem(N, H, E, top_k, two_i // 2, 0, x.dtype)
+    if act is None:
+        act = torch.empty((grouping.max_rows, two_i // 2), dtype=x.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_gate_up(ctypes.byref(p), _ptr(x), _ptr(w_gate_up), _ptr(grouping.sorted_pairs),
+                                          _ptr(grouping.tile_expert), _ptr(grouping.tile_rows),
+                                          _ptr(grouping.num_tiles), grouping.block_m, grouping.max_tiles,
+                                          _ptr(act), _stream(dev)))
+    return act
+
+
+def moe_down(act, w_down, topk_w, grouping: Grouping, num_tokens: int, top_k: int, y=None):
+    """y [N*k, H] in act.dtype: y[p] = topk_w[p] * (act[row of p] . w_down[e]^T)."""
+    act = _gpu(act, "act")
+    dev = act.device
+    w_down = _gpu(w_down, "w_down", act.dtype, dev)
+    topk_w = _gpu(topk_w, "topk_w", torch.float32, dev)
+    E, H, I = w_down.shape
+    p = problem(num_tokens, H, E, top_k, I, 0, act.dtype)
+    if y is None:
+        y = torch.empty((num_tokens * top_k, H), dtype=act.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_down(ctypes.byref(p), _ptr(act), _ptr(w_down), _ptr(topk_w),
+                                       _ptr(grouping.sorted_pairs), _ptr(grouping.tile_expert),
+                                       _ptr(grouping.tile_rows), _ptr(grouping.num_tiles), grouping.block_m,
+                                       grouping.max_tiles, _ptr(y), _stream(dev)))
+    return y
+
+
+def moe_shared_expert(x, shared_w_gate_up, shared_w_down, shared_scale, shared_act=None, shared_y=None):
+    """(shared_act [N, I_s], shared_y [N, H] = shared_scale[:, None] * SwiGLU_s(x))."""
+    x = _gpu(x, "x")
+    dev = x.device
+    shared_w_gate_up = _gpu(shared_w_gate_up, "shared_w_gate_up", x.dtype, dev)
+    shared_w_down = _gpu(shared_w_down, "shared_w_down", x.dtype, dev)
+    shared_scale = _gpu(shared_scale, "shared_scale", torch.float32, dev)
+    N, H = x.shape
+    Is = shared_w_gate_up.shape[0] // 2
+    p = problem(N, H, 1, 1, 1, Is, x.dtype)
+    if shared_act is None:
+        shared_act = torch.empty((N, Is), dtype=x.dtype, device=dev)
+    if shared_y is None:
+        shared_y = torch.empty((N, H), dtype=x.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_shared_expert(ctypes.byref(p), _ptr(x), _ptr(shared_w_gate_up),
+                                                _ptr(shared_w_down), _ptr(shared_scale), _ptr(shared_act),
+                                                _ptr(shared_y), _stream(dev)))
+    return shared_act, shared_y
+
+
+def moe_combine(y, num_tokens: int, top_k: int, shared_y=None, out=None):
+    """out [N, H] = sum over the k slot rows of y (+ shared_y)."""
+    y = _gpu(y, "y")
+    dev = y.device
+    H = y.shape[1]
+    if shared_y is not None:
+        shared_y = _gpu(shared_y, "shared_y", y.dtype, dev)
+    p = problem(num_tokens, H, top_k, top_k, 1, 0, y.dtype)
+    if out is None:
+        out = torch.empty((num_tokens, H), dtype=y.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_combine(ctypes.byref(p), _ptr(y), _ptr(shared_y), _ptr(out), _stream(dev)))
+    return out
+
+
+_workspaces = {}
+
+
+def workspace_for(p: MoEProblem, device) -> torch.Tensor:
+    """A cached uint8 workspace large enough for `p` on `device`."""
+    need = moe_workspace_size(p)
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
+def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob=True, shared_w_gate_up=None,
+                shared_w_down=None, shared_gate=None, out=None, workspace=None):
+    """The whole block: out [N, H] in x.dtype."""
+    x = _gpu(x, "x")
+    dev = x.device
+    for t, n in ((router_w, "router_w"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
+        _gpu(t, n, x.dtype, dev)
+    for t, n in ((shared_w_gate_up, "shared_w_gate_up"), (shared_w_down, "shared_w_down"),
+                 (shared_gate, "shared_gate")):
+        if t is not None:
+            _gpu(t, n, x.dtype, dev)
+    p = problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = workspace_for(p, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_forward(ctypes.byref(p), _ptr(x), _ptr(router_w), _ptr(w_gate_up), _ptr(w_down),
+                                          _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(shared_gate),
+                                          _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out

@@ -1,0 +1,309 @@
+// Grouped expert products of the MoE block.
+//
+//   gate/up: for every tile row r holding pair p (token p / k, expert e)
+//              act[r, i] = silu(x[tok] . Wg[e, i]) * (x[tok] . Wu[e, i])
+//   down:    y[p, h] = scale[p] * (act[r] . Wd[e, h])
+//
+// "M03 · Sparse MoE：路由、按 expert 分组计算、shared expert", 题面速览 (expert
+// formula, one product per expert over its gathered tokens) and L1 细节
+// (Wg, Wu are [I, H], Wd is [H, I]); the gate rows precede the up rows in the
+// packed gate/up weight.  The routing-weight multiply in the down epilogue is
+// the expert-output scaling of "Nano-vLLM 代码笔记 (八)",
+// Qwen3MoeSparseMoeBlock forward.
+//
+// Tiles come from the align kernel: tile t is rows [t*BM, (t+1)*BM) of the
+// padded pair list, all of one expert.  The launch covers an upper bound of
+// tiles; workgroups past the device-side tile count return at once, so the
+// host never reads the count.
+//
+// bf16 kernel (gfx950): C = A . B^T with A gathered rows [BM, K] and B the
+// expert's weight rows [BN, K], both K-contiguous.  64-wide K steps are
+// staged through LDS, double buffered (global loads of step s+1 in flight
+// while the matrix cores work on step s), 128-byte rows with their 16-byte
+// chunks XOR-swizzled by row so fragment reads hit distinct banks.  Each wave
+// owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 16x16x32 bf16 MFMAs with
+// float32 accumulators.  For gate/up a B tile holds BN/2 gate rows and the
+// matching BN/2 up rows, and each wave holds matching gate and up columns in
+// the same lanes, so the SwiGLU is computed in registers.  Launch order puts
+// the tiles of one expert and column block next to each other on one XCD, so
+// they meet the same weight tile in that XCD's L2.
+//
+// fp32 kernel: plain FMA loops, any shape (used for float32 layers).
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+
+constexpr int kBK = 64;          // K elements per stage (128 bytes of bf16)
+constexpr int kChunksPerRow = kBK / 8;
+
+enum { kGateUp = 0, kDown = 1 };
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kBK + ((chunk ^ (row & 7)) << 3);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
+  constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M;
+  constexpr int WN = BN / WAVES_N;
+  constexpr int TM = WM / 16;
+  constexpr int TN = WN / 16;
+  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+  static_assert(MODE != kGateUp || TN % 2 == 0, "gate/up needs matching gate and up sub-tiles");
+  constexpr int kAChunks = BM * kChunksPerRow;
+  constexpr int kBChunks = BN * kChunksPerRow;
+  constexpr int kALoads = (kAChunks + kThreads - 1) / kThreads;
+  constexpr int kBLoads = (kBChunks + kThreads - 1) / kThreads;
+
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][(BM + BN) * kBK];
+
+  const bool grouped = g.sorted_pairs != nullptr;
+  const int n_tiles_n = (MODE == kGateUp) ? g.n_out / (BN / 2) : (g.n_out + BN - 1) / BN;
+  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int mt = logical % g.max_tiles;
+  const int nt = logical / g.max_tiles;
+  if (nt >= n_tiles_n) return;
+  int rows_valid, expert;
+  if (grouped) {
+    if (mt >= *g.num_tiles) return;
+    rows_valid = g.tile_rows[mt];
+    expert = g.tile_expert[mt];
+  } else {
+    rows_valid = min(BM, g.dense_rows - mt * BM);
+    if (rows_valid <= 0) return;
+    expert = 0;
+  }
+  const int row0 = mt * BM;
+  const int K = g.K;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / 64;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+
+  const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.a);
+  const uint16_t* __restrict__ B =
+      static_cast<const uint16_t*>(g.b) + (int64_t)expert * g.expert_stride;
+
+  // Per-thread global sources of its A and B chunks (fixed over K).
+  const uint16_t* a_src[kALoads];
+  int a_dst[kALoads];
+#pragma unroll
+  for (int i = 0; i < kALoads; ++i) {
+    const int c = tid + i * kThreads;
+    const int r = c / kChunksPerRow, ch = c % kChunksPerRow;
+    a_dst[i] = (c < kAChunks) ? swz(r, ch) : -1;
+    int64_t src_row;
+    if (MODE == kGateUp) {
+      if (grouped) {
+        const int pr = (c < kAChunks) ? g.sorted_pairs[row0 + r] : g.num_pairs;
+        src_row = (pr < g.num_pairs) ? pr / g.top_k : 0;       // sentinel rows read token 0
+      } else {
+        src_row = min(row0 + r, g.dense_rows - 1);
+      }
+    } else {
+      src_row = grouped ? (row0 + r) : min(row0 + r, g.dense_rows - 1);
+    }
+    a_src[i] = A + src_row * K + ch * 8;
+  }
+  const uint16_t* b_src[kBLoads];
+  int b_dst[kBLoads];
+#pragma unroll
+  for (int i = 0; i < kBLoads; ++i) {
+    const int c = tid + i * kThreads;
+    const int j = c / kChunksPerRow, ch = c % kChunksPerRow;
+    b_dst[i] = (c < kBChunks) ? swz(j, ch) : -1;
+    int64_t wrow;
+    if (MODE == kGateUp) {
+      const int half = BN / 2;
+      wrow = (j < half) ? (int64_t)nt * half + j : (int64_t)g.n_out + nt * half + (j - half);
+    } else {
+      wrow = (int64_t)nt * BN + j;
+      if (wrow >= g.n_out) b_dst[i] = -2 - b_dst[i];           // outside: store zeros
+    }
+    b_src[i] = B + min(wrow, (int64_t)(MODE == kGateUp ? 2 * g.n_out : g.n_out) - 1) * K + ch * 8;
+  }
+
+  floatx4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[kALoads], rb[kBLoads];
+  auto load_stage = [&](int kt) {
+    const int koff = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i)
+      if (a_dst[i] >= 0) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + koff);
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i)
+      if (b_dst[i] >= 0) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + koff);
+  };
+  auto store_stage = [&](int st) {
+    uint16_t* As = smem[st];
+    uint16_t* Bs = smem[st] + BM * kBK;
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i)
+      if (a_dst[i] >= 0) *reinterpret_cast<uint4*>(As + a_dst[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) {
+      if (b_dst[i] >= 0) *reinterpret_cast<uint4*>(Bs + b_dst[i]) = rb[i];
+      else if (b_dst[i] <= -2) *reinterpret_cast<uint4*>(Bs + (-2 - b_dst[i])) = uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  // Row of the B tile read by sub-tile tn of this wave.
+  auto b_tile_row = [&](int tn) {
+    if (MODE == kGateUp) {
+      constexpr int kHalfTN = TN / 2;
+      const int part = tn / kHalfTN, t = tn % kHalfTN;
+      return part * (BN / 2) + wn * (WN / 2) + t * 16 + (lane & 15);
+    }
+    return wn * WN + tn * 16 + (lane & 15);
+  };
+
+  const int nk = K / kBK;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load_stage(kt + 1);
+    const uint16_t* As = smem[kt & 1];
+    const uint16_t* Bs = smem[kt & 1] + BM * kBK;
+#pragma unroll
+    for (int kk = 0; kk < kBK / 32; ++kk) {
+      const int ch = kk * 4 + (lane >> 4);
+      uint4 af[TM], bfr[TN];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const int r = wm * WM + tm * 16 + (lane & 15);
+        af[tm] = *reinterpret_cast<const uint4*>(As + swz(r, ch));
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz(b_tile_row(tn), ch));
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(af[tm], bfr[tn], acc[tm][tn]);
+    }
+    if (kt + 1 < nk) store_stage((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: lane holds rows 4*(lane/16)+i of column lane%16 of each sub-tile.
+  uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * WM + tm * 16 + (lane >> 4) * 4 + i;
+      if (r >= rows_valid) continue;
+      if (MODE == kGateUp) {
+        constexpr int kHalfTN = TN / 2;
+        uint16_t* out_row = C + (int64_t)(row0 + r) * g.n_out;
+#pragma unroll
+        for (int t = 0; t < kHalfTN; ++t) {
+          const int col = nt * (BN / 2) + wn * (WN / 2) + t * 16 + (lane & 15);
+          const float gv = acc[tm][t][i], uv = acc[tm][t + kHalfTN][i];
+          out_row[col] = f32_to_bf16(silu_f32(gv) * uv);
+        }
+      } else {
+        const int prow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
+        const float sc = g.scale[prow];
+        uint16_t* out_row = C + (int64_t)prow * g.n_out;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int col = nt * BN + wn * WN + tn * 16 + (lane & 15);
+          if (col < g.n_out) out_row[col] = f32_to_bf16(sc * acc[tm][tn][i]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- float32
+
+constexpr int kF32Cols = 64;
+constexpr int kF32Threads = 256;
+
+template <int MODE>
+__global__ __launch_bounds__(kF32Threads) void grouped_gemm_f32_kernel(GemmProblem g) {
+  const bool grouped = g.sorted_pairs != nullptr;
+  const int mt = blockIdx.x;
+  const int col = blockIdx.y * kF32Cols + (threadIdx.x % kF32Cols);
+  int rows_valid, expert;
+  if (grouped) {
+    if (mt >= *g.num_tiles) return;
+    rows_valid = g.tile_rows[mt];
+    expert = g.tile_expert[mt];
+  } else {
+    rows_valid = min(g.block_m, g.dense_rows - mt * g.block_m);
+    if (rows_valid <= 0) return;
+    expert = 0;
+  }
+  if (col >= g.n_out) return;
+  const float* A = static_cast<const float*>(g.a);
+  const float* B = static_cast<const float*>(g.b) + (int64_t)expert * g.expert_stride;
+  float* C = static_cast<float*>(g.c);
+  const int K = g.K;
+  const int row0 = mt * g.block_m;
+  for (int r = threadIdx.x / kF32Cols; r < rows_valid; r += kF32Threads / kF32Cols) {
+    if (MODE == kGateUp) {
+      int64_t tok = row0 + r;
+      if (grouped) tok = g.sorted_pairs[row0 + r] / g.top_k;
+      const float* xr = A + tok * K;
+      const float* wg = B + (int64_t)col * K;
+      const float* wu = B + (int64_t)(g.n_out + col) * K;
+      float gv = 0.f, uv = 0.f;
+      for (int h = 0; h < K; ++h) {
+        gv = fmaf(xr[h], wg[h], gv);
+        uv = fmaf(xr[h], wu[h], uv);
+      }
+      C[(int64_t)(row0 + r) * g.n_out + col] = silu_f32(gv) * uv;
+    } else {
+      const int64_t prow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
+      const float* ar = A + (int64_t)(row0 + r) * K;
+      const float* wd = B + (int64_t)col * K;
+      float acc = 0.f;
+      for (int i = 0; i < K; ++i) acc = fmaf(ar[i], wd[i], acc);
+      C[prow * g.n_out + col] = g.scale[prow] * acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE>
+static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
+  const int n_tiles_n = (MODE == kGateUp) ? g.n_out / (BN / 2) : (g.n_out + BN - 1) / BN;
+  const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, MODE>), dim3((unsigned)blocks),
+                     dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
+  if (g.dtype == MOE_F32) {
+    const dim3 grid(g.max_tiles, (g.n_out + kF32Cols - 1) / kF32Cols);
+    if (grid.x == 0) return hipSuccess;
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<MODE>, grid, dim3(kF32Threads), 0, s, g);
+    return hipGetLastError();
+  }
+  switch (g.block_m) {
+    case 16: return launch_bf16<16, 128, 1, 4, MODE>(g, s);
+    case 32: return launch_bf16<32, 128, 1, 4, MODE>(g, s);
+    case 64: return launch_bf16<64, 128, 2, 2, MODE>(g, s);
+    case 128: return launch_bf16<128, 128, 2, 2, MODE>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s) { return launch_mode<kGateUp>(g, s); }
+hipError_t launch_down(const GemmProblem& g, hipStream_t s) { return launch_mode<kDown>(g, s); }
+
+}  // namespace moe

@@ -1,0 +1,349 @@
+// C ABI of the MoE block: argument validation, workspace layout and the
+// stream-ordered launch sequence.  Every check runs on the host before any
+// HIP call; no call synchronises or reads device memory on the host.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "moe_launch.h"
+#include "moe_mi355x.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+size_t elt_size(int32_t dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// What a call reads of moe_problem; fields a call does not use are not checked.
+enum : unsigned { kUsesExperts = 1, kUsesInter = 2, kUsesShared = 4, kUsesAll = 7 };
+
+int check_problem(const moe_problem* p, unsigned uses = kUsesAll) {
+  if (!p) return fail(MOE_EINVAL, "problem is NULL");
+  if (p->num_tokens < 0) return fail(MOE_EINVAL, "num_tokens must be >= 0");
+  if (p->hidden < 1) return fail(MOE_EINVAL, "hidden must be >= 1");
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "unknown dtype");
+  if (p->top_k < 1) return fail(MOE_EINVAL, "top_k must be >= 1");
+  if (p->top_k > moe::kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", moe::kMaxTopK);
+  const int64_t lim = (int64_t)1 << 30;
+  if (p->num_tokens > lim || p->hidden > lim || p->num_tokens * p->top_k >= lim ||
+      p->num_tokens * p->top_k * p->hidden >= ((int64_t)1 << 40))
+    return fail(MOE_EUNSUPPORTED, "sizes too large");
+  if (p->dtype == MOE_BF16 && p->hidden % 64)
+    return fail(MOE_EUNSUPPORTED, "bf16 needs hidden to be a multiple of 64");
+  if (uses & kUsesExperts) {
+    if (p->num_experts < 1) return fail(MOE_EINVAL, "num_experts must be >= 1");
+    if (p->top_k > p->num_experts)
+      return fail(MOE_EINVAL, "top_k=%lld outside [1, num_experts=%lld]", (long long)p->top_k,
+                  (long long)p->num_experts);
+    if (p->num_experts > moe::kMaxExperts)
+      return fail(MOE_EUNSUPPORTED, "num_experts > %d", moe::kMaxExperts);
+    if (p->norm_topk_prob != 0 && p->norm_topk_prob != 1)
+      return fail(MOE_EINVAL, "norm_topk_prob must be 0 or 1");
+  }
+  if (uses & kUsesInter) {
+    if (p->inter < 1 || p->inter > lim) return fail(MOE_EINVAL, "inter must be in [1, 2^30]");
+    if (p->dtype == MOE_BF16 && p->inter % 64)
+      return fail(MOE_EUNSUPPORTED, "bf16 needs inter to be a multiple of 64");
+  }
+  if (uses & kUsesShared) {
+    if (p->shared_inter < 0 || p->shared_inter > lim) return fail(MOE_EINVAL, "shared_inter must be in [0, 2^30]");
+    if (p->dtype == MOE_BF16 && p->shared_inter % 64)
+      return fail(MOE_EUNSUPPORTED, "bf16 needs shared_inter to be a multiple of 64");
+  }
+  return MOE_OK;
+}
+
+int64_t choose_block_m(const moe_problem* p) {
+  if (p->dtype == MOE_F32) return 16;
+  const double avg = (double)(p->num_tokens * p->top_k) / (double)p->num_experts;
+  if (avg < 24) return 16;
+  if (avg < 48) return 32;
+  if (avg < 96) return 64;
+  return 128;
+}
+
+bool block_m_supported(int32_t dtype, int64_t bm) {
+  if (dtype == MOE_F32) return bm >= 1 && bm <= 1024;
+  return bm == 16 || bm == 32 || bm == 64 || bm == 128;
+}
+
+void capacity(int64_t pairs, int64_t experts, int64_t bm, int64_t* rows, int64_t* tiles) {
+  const int64_t t = (pairs + std::min(experts, pairs) * (bm - 1)) / bm;
+  *tiles = t;
+  *rows = t * bm;
+}
+
+void layout_of(const moe_problem* p, moe_workspace_layout* L) {
+  memset(L, 0, sizeof(*L));
+  const int64_t N = p->num_tokens, P = N * p->top_k, E = p->num_experts;
+  const size_t es = elt_size(p->dtype);
+  L->block_m = choose_block_m(p);
+  capacity(P, E, L->block_m, &L->max_rows, &L->max_tiles);
+  size_t off = 0;
+  auto region = [&](size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    const size_t r = off;
+    off += bytes;
+    return r;
+  };
+  L->topk_ids = region(P * 4);
+  L->topk_w = region(P * 4);
+  L->shared_scale = region(p->shared_inter ? N * 4 : 0);
+  L->counts = region(E * 4);
+  L->offsets = region((E + 1) * 4);
+  L->order = region(P * 4);
+  L->sorted_pairs = region(L->max_rows * 4);
+  L->tile_expert = region(L->max_tiles * 4);
+  L->tile_rows = region(L->max_tiles * 4);
+  L->num_tiles = region(4);
+  L->act = region(L->max_rows * p->inter * es);
+  L->y = region(P * p->hidden * es);
+  L->shared_act = region(N * p->shared_inter * es);
+  L->shared_y = region(p->shared_inter ? N * p->hidden * es : 0);
+  L->total_bytes = (off + 255) & ~(size_t)255;
+}
+
+moe::GemmProblem gemm_common(const moe_problem* p) {
+  moe::GemmProblem g;
+  memset(&g, 0, sizeof(g));
+  g.top_k = (int32_t)p->top_k;
+  g.num_pairs = (int32_t)(p->num_tokens * p->top_k);
+  g.dtype = p->dtype;
+  return g;
+}
+
+int check_ptrs_bf16(const moe_problem* p, std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if (q && p->dtype == MOE_BF16 && !aligned16(q))
+      return fail(MOE_EUNSUPPORTED, "bf16 tensors must be 16-byte aligned");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_align_capacity(int64_t num_pairs, int64_t num_experts, int64_t block_m, int64_t* max_rows,
+                       int64_t* max_tiles) {
+  if (!max_rows || !max_tiles) return fail(MOE_EINVAL, "output pointer is NULL");
+  if (num_pairs < 0 || num_experts < 1 || block_m < 1)
+    return fail(MOE_EINVAL, "need num_pairs >= 0, num_experts >= 1, block_m >= 1");
+  capacity(num_pairs, num_experts, block_m, max_rows, max_tiles);
+  return ok();
+}
+
+int moe_get_workspace_layout(const moe_problem* p, moe_workspace_layout* layout) {
+  if (int rc = check_problem(p)) return rc;
+  if (!layout) return fail(MOE_EINVAL, "layout is NULL");
+  layout_of(p, layout);
+  return ok();
+}
+
+int moe_workspace_size(const moe_problem* p, size_t* bytes) {
+  if (int rc = check_problem(p)) return rc;
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  moe_workspace_layout L;
+  layout_of(p, &L);
+  *bytes = L.total_bytes;
+  return ok();
+}
+
+int moe_route(const moe_problem* p, const void* x, const void* router_w, const void* shared_gate,
+              int32_t* topk_ids, float* topk_w, float* shared_scale, void* stream) {
+  if (int rc = check_problem(p, kUsesExperts)) return rc;
+  if (p->num_tokens == 0) return ok();
+  if (!x || !router_w || !topk_ids || !topk_w) return fail(MOE_EINVAL, "NULL tensor");
+  if (shared_gate && !shared_scale) return fail(MOE_EINVAL, "shared_gate given without shared_scale");
+  if (int rc = check_ptrs_bf16(p, {x, router_w, shared_gate})) return rc;
+  if (int rc = hip_status(moe::launch_route(*p, x, router_w, shared_gate, topk_ids, topk_w,
+                                            shared_scale, (hipStream_t)stream), "route"))
+    return rc;
+  return ok();
+}
+
+int moe_align(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k, int64_t num_experts,
+              int64_t block_m, int32_t* counts, int32_t* offsets, int32_t* order,
+              int32_t* sorted_pairs, int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles,
+              void* stream) {
+  if (num_tokens < 0 || top_k < 1 || num_experts < 1) return fail(MOE_EINVAL, "bad sizes");
+  if (num_experts > moe::kMaxExperts) return fail(MOE_EUNSUPPORTED, "num_experts > %d", moe::kMaxExperts);
+  if (block_m < 1 || block_m > 1024) return fail(MOE_EINVAL, "block_m outside [1, 1024]");
+  if (num_tokens * top_k >= ((int64_t)1 << 30)) return fail(MOE_EUNSUPPORTED, "too many pairs");
+  if (!counts || !offsets || !num_tiles) return fail(MOE_EINVAL, "NULL output");
+  if (num_tokens > 0 && (!topk_ids || !order || !sorted_pairs || !tile_expert || !tile_rows))
+    return fail(MOE_EINVAL, "NULL tensor");
+  if (int rc = hip_status(moe::launch_align(topk_ids, num_tokens * top_k, num_experts, block_m, counts,
+                                            offsets, order, sorted_pairs, tile_expert, tile_rows,
+                                            num_tiles, (hipStream_t)stream), "align"))
+    return rc;
+  return ok();
+}
+
+int moe_gate_up(const moe_problem* p, const void* x, const void* w_gate_up, const int32_t* sorted_pairs,
+                const int32_t* tile_expert, const int32_t* tile_rows, const int32_t* num_tiles,
+                int64_t block_m, int64_t max_tiles, void* act, void* stream) {
+  if (int rc = check_problem(p, kUsesExperts | kUsesInter)) return rc;
+  if (p->num_tokens == 0) return ok();
+  if (!x || !w_gate_up || !sorted_pairs || !tile_expert || !tile_rows || !num_tiles || !act)
+    return fail(MOE_EINVAL, "NULL tensor");
+  if (!block_m_supported(p->dtype, block_m)) return fail(MOE_EUNSUPPORTED, "block_m %lld", (long long)block_m);
+  if (max_tiles < 0 || max_tiles >= ((int64_t)1 << 24)) return fail(MOE_EINVAL, "bad max_tiles");
+  if (int rc = check_ptrs_bf16(p, {x, w_gate_up, act})) return rc;
+  moe::GemmProblem g = gemm_common(p);
+  g.a = x;
+  g.b = w_gate_up;
+  g.sorted_pairs = sorted_pairs;
+  g.tile_expert = tile_expert;
+  g.tile_rows = tile_rows;
+  g.num_tiles = num_tiles;
+  g.c = act;
+  g.expert_stride = 2 * p->inter * p->hidden;
+  g.K = (int32_t)p->hidden;
+  g.n_out = (int32_t)p->inter;
+  g.block_m = (int32_t)block_m;
+  g.max_tiles = (int32_t)max_tiles;
+  return hip_status(moe::launch_gate_up(g, (hipStream_t)stream), "gate_up") ?: ok();
+}
+
+int moe_down(const moe_problem* p, const void* act, const void* w_down, const float* topk_w,
+             const int32_t* sorted_pairs, const int32_t* tile_expert, const int32_t* tile_rows,
+             const int32_t* num_tiles, int64_t block_m, int64_t max_tiles, void* y, void* stream) {
+  if (int rc = check_problem(p, kUsesExperts | kUsesInter)) return rc;
+  if (p->num_tokens == 0) return ok();
+  if (!act || !w_down || !topk_w || !sorted_pairs || !tile_expert || !tile_rows || !num_tiles || !y)
+    return fail(MOE_EINVAL, "NULL tensor");
+  if (!block_m_supported(p->dtype, block_m)) return fail(MOE_EUNSUPPORTED, "block_m %lld", (long long)block_m);
+  if (max_tiles < 0 || max_tiles >= ((int64_t)1 << 24)) return fail(MOE_EINVAL, "bad max_tiles");
+  if (int rc = check_ptrs_bf16(p, {act, w_down, y})) return rc;
+  moe::GemmProblem g = gemm_common(p);
+  g.a = act;
+  g.b = w_down;
+  g.sorted_pairs = sorted_pairs;
+  g.tile_expert = tile_expert;
+  g.tile_rows = tile_rows;
+  g.num_tiles = num_tiles;
+  g.scale = topk_w;
+  g.c = y;
+  g.expert_stride = p->hidden * p->inter;
+  g.K = (int32_t)p->inter;
+  g.n_out = (int32_t)p->hidden;
+  g.block_m = (int32_t)block_m;
+  g.max_tiles = (int32_t)max_tiles;
+  return hip_status(moe::launch_down(g, (hipStream_t)stream), "down") ?: ok();
+}
+
+int moe_shared_expert(const moe_problem* p, const void* x, const void* shared_w_gate_up,
+                      const void* shared_w_down, const float* shared_scale, void* shared_act,
+                      void* shared_y, void* stream) {
+  if (int rc = check_problem(p, kUsesShared)) return rc;
+  if (p->shared_inter < 1) return fail(MOE_EINVAL, "shared_inter must be >= 1 for the shared expert");
+  if (p->num_tokens == 0) return ok();
+  if (!x || !shared_w_gate_up || !shared_w_down || !shared_scale || !shared_act || !shared_y)
+    return fail(MOE_EINVAL, "NULL tensor");
+  if (int rc = check_ptrs_bf16(p, {x, shared_w_gate_up, shared_w_down, shared_act, shared_y})) return rc;
+  const int64_t N = p->num_tokens;
+  const int64_t bm = p->dtype == MOE_F32 ? 16 : 128;
+  moe::GemmProblem g = gemm_common(p);
+  g.dense_rows = (int32_t)N;
+  g.block_m = (int32_t)bm;
+  g.max_tiles = (int32_t)((N + bm - 1) / bm);
+  g.a = x;
+  g.b = shared_w_gate_up;
+  g.c = shared_act;
+  g.K = (int32_t)p->hidden;
+  g.n_out = (int32_t)p->shared_inter;
+  if (int rc = hip_status(moe::launch_gate_up(g, (hipStream_t)stream), "shared gate_up")) return rc;
+  g.a = shared_act;
+  g.b = shared_w_down;
+  g.c = shared_y;
+  g.scale = shared_scale;
+  g.K = (int32_t)p->shared_inter;
+  g.n_out = (int32_t)p->hidden;
+  return hip_status(moe::launch_down(g, (hipStream_t)stream), "shared down") ?: ok();
+}
+
+int moe_combine(const moe_problem* p, const void* y, const void* shared_y, void* out, void* stream) {
+  if (int rc = check_problem(p, 0)) return rc;
+  if (p->num_tokens == 0) return ok();
+  if (!y || !out) return fail(MOE_EINVAL, "NULL tensor");
+  if (int rc = check_ptrs_bf16(p, {y, shared_y, out})) return rc;
+  return hip_status(moe::launch_combine(y, shared_y, out, p->num_tokens, p->hidden, p->top_k,
+                                        p->dtype, (hipStream_t)stream), "combine") ?: ok();
+}
+
+int moe_forward(const moe_problem* p, const void* x, const void* router_w, const void* w_gate_up,
+                const void* w_down, const void* shared_w_gate_up, const void* shared_w_down,
+                const void* shared_gate, void* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  if (int rc = check_problem(p)) return rc;
+  const bool shared = shared_w_gate_up != nullptr;
+  if (shared != (p->shared_inter > 0))
+    return fail(MOE_EINVAL, "shared_w_gate_up must be given exactly when shared_inter > 0");
+  if (shared && (!shared_w_down || !shared_gate)) return fail(MOE_EINVAL, "shared expert needs all three tensors");
+  if (p->num_tokens == 0) return ok();
+  if (!x || !router_w || !w_gate_up || !w_down || !out || !workspace) return fail(MOE_EINVAL, "NULL tensor");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_EUNSUPPORTED, "workspace must be 256-byte aligned");
+  moe_workspace_layout L;
+  layout_of(p, &L);
+  if (workspace_bytes < L.total_bytes)
+    return fail(MOE_ENOSPC, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total_bytes);
+  if (int rc = check_ptrs_bf16(p, {x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down,
+                                   shared_gate, out}))
+    return rc;
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
+  int32_t* ids = (int32_t*)at(L.topk_ids);
+  float* w = (float*)at(L.topk_w);
+  float* sscale = shared ? (float*)at(L.shared_scale) : nullptr;
+  if (int rc = moe_route(p, x, router_w, shared ? shared_gate : nullptr, ids, w, sscale, stream)) return rc;
+  int32_t* sorted = (int32_t*)at(L.sorted_pairs);
+  int32_t* texp = (int32_t*)at(L.tile_expert);
+  int32_t* trows = (int32_t*)at(L.tile_rows);
+  int32_t* ntiles = (int32_t*)at(L.num_tiles);
+  if (int rc = moe_align(ids, p->num_tokens, p->top_k, p->num_experts, L.block_m, (int32_t*)at(L.counts),
+                         (int32_t*)at(L.offsets), (int32_t*)at(L.order), sorted, texp, trows, ntiles,
+                         stream))
+    return rc;
+  if (int rc = moe_gate_up(p, x, w_gate_up, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
+                           at(L.act), stream))
+    return rc;
+  if (int rc = moe_down(p, at(L.act), w_down, w, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
+                        at(L.y), stream))
+    return rc;
+  if (shared) {
+    if (int rc = moe_shared_expert(p, x, shared_w_gate_up, shared_w_down, sscale, at(L.shared_act),
+                                   at(L.shared_y), stream))
+      return rc;
+  }
+  if (int rc = moe_combine(p, at(L.y), shared ? at(L.shared_y) : nullptr, out, stream)) return rc;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_mi355x.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+
+// Router: logits, float32 softmax, top-k, optional renormalisation and the
+// optional shared-expert gate.
+hipError_t launch_route(const moe_problem& p, const void* x, const void* router_w,
+                        const void* shared_gate, int32_t* ids, float* w, float* shared_scale,
+                        hipStream_t s);
+
+// Stable grouping of the pairs by expert, padded to block_m.
+hipError_t launch_align(const int32_t* ids, int64_t num_pairs, int64_t num_experts, int64_t block_m,
+                        int32_t* counts, int32_t* offsets, int32_t* order, int32_t* sorted_pairs,
+                        int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles, hipStream_t s);
+
+// One grouped (or dense, when sorted_pairs == nullptr) product.
+struct GemmProblem {
+  const void* a;               // gate/up: x [N, K];  down: act [rows, K]
+  const void* b;               // expert weights, expert e at b + e * expert_stride
+  const int32_t* sorted_pairs; // nullptr: dense rows 0..dense_rows-1, expert 0
+  const int32_t* tile_expert;
+  const int32_t* tile_rows;
+  const int32_t* num_tiles;
+  const float* scale;          // down only: per-pair (grouped) or per-row (dense) factor
+  void* c;                     // gate/up: act [rows, Nout];  down: y [pairs or rows, Nout]
+  int64_t expert_stride;       // elements
+  int32_t K;                   // reduction length
+  int32_t n_out;               // gate/up: I (act columns);  down: H
+  int32_t top_k;
+  int32_t num_pairs;           // sentinel value
+  int32_t dense_rows;
+  int32_t block_m;
+  int32_t max_tiles;
+  int32_t dtype;               // MOE_F32 / MOE_BF16
+};
+
+hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s);
+hipError_t launch_down(const GemmProblem& g, hipStream_t s);
+
+// out[n] = sum_j y[n*k + j] (+ shared_y[n]), float32 sum in slot order.
+hipError_t launch_combine(const void* y, const void* shared_y, void* out, int64_t N, int64_t H,
+                          int64_t top_k, int32_t dtype, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,91 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_ffn_amd as moe
+from sparse_moe_ffn_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_mi355x.h")
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = moe.load_library()
+    names = declared()
+    assert "moe_forward" in names and "moe_route" in names and "moe_align" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_problem_validation_codes():
+    P = moe.problem
+    ok = P(4096, 2048, 128, 8, 768)
+    assert moe.moe_workspace_size(ok) > 0
+    for bad, code in ((P(4, 64, 4, 5, 64), B.MOE_EINVAL), (P(4, 64, 4, 0, 64), B.MOE_EINVAL),
+                      (P(-1, 64, 4, 2, 64), B.MOE_EINVAL), (P(4, 100, 4, 2, 64), B.MOE_EUNSUPPORTED),
+                      (P(4, 64, 4, 2, 96), B.MOE_EUNSUPPORTED), (P(4, 64, 600, 2, 64), B.MOE_EUNSUPPORTED),
+                      (P(4, 64, 64, 33, 64), B.MOE_EUNSUPPORTED), (P(4, 64, 4, 2, 64, shared_inter=32), B.MOE_EUNSUPPORTED)):
+        with pytest.raises(B.MoEError) as ei:
+            moe.moe_workspace_size(bad)
+        assert ei.value.code == code, (bad.top_k, ei.value)
+    # fp32 takes any shape
+    assert moe.moe_workspace_size(P(3, 1, 3, 2, 1, dtype=__import__("torch").float32)) > 0
+
+
+def test_workspace_layout_is_ordered_and_aligned():
+    for args in ((4096, 2048, 128, 8, 768), (64, 2048, 128, 8, 768), (8192, 2048, 128, 8, 768, 2048), (7, 64, 5, 3, 64)):
+        L = moe.moe_get_workspace_layout(moe.problem(*args))
+        offs = [L[k] for k in ("topk_ids", "topk_w", "shared_scale", "counts", "offsets", "order", "sorted_pairs",
+                               "tile_expert", "tile_rows", "num_tiles", "act", "y", "shared_act", "shared_y")]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        assert L["total_bytes"] >= offs[-1] and L["total_bytes"] % 256 == 0
+        assert L["max_rows"] == L["max_tiles"] * L["block_m"]
+
+
+def test_block_m_follows_rows_per_expert():
+    bm = lambda N: moe.moe_get_workspace_layout(moe.problem(N, 2048, 128, 8, 768))["block_m"]
+    assert (bm(64), bm(4096), bm(16384)) == (16, 128, 128)
+
+
+@pytest.mark.parametrize("pairs,E,bm", [(6, 5, 2), (512, 128, 16), (32768, 128, 128), (3, 10, 64), (0, 4, 16)])
+def test_align_capacity_bounds_every_grouping(pairs, E, bm):
+    rows, tiles = moe.moe_align_capacity(pairs, E, bm)
+    assert rows == tiles * bm
+    # the worst case: as many experts as possible with one pair past a tile boundary
+    m = min(E, pairs)
+    worst = 0
+    if m:
+        base, extra = divmod(pairs, m)
+        worst = sum(-(-(base + (i < extra)) // bm) for i in range(m))
+    assert tiles >= worst
+
+
+def test_forward_rejects_before_any_hip_call():
+    lib = moe.load_library()
+    p = moe.problem(16, 64, 4, 2, 64)
+    fake = ctypes.c_void_p(1 << 20)
+    rc = lib.moe_forward(ctypes.byref(p), fake, fake, fake, fake, None, None, None, fake, fake, 16, None)
+    assert rc == B.MOE_ENOSPC and b"workspace" in lib.moe_last_error()
+    rc = lib.moe_forward(ctypes.byref(p), None, fake, fake, fake, None, None, None, fake, fake, 1 << 30, None)
+    assert rc == B.MOE_EINVAL
+    rc = lib.moe_forward(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, fake, fake, 1 << 30, None)
+    assert rc == B.MOE_EINVAL                               # shared weights without shared_inter
+    rc = lib.moe_forward(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, None, None, None,
+                         fake, fake, 1 << 30, None)
+    assert rc == B.MOE_EUNSUPPORTED                          # misaligned bf16
+    rc = lib.moe_align(fake, 4, 2, 4, 0, fake, fake, fake, fake, fake, fake, fake, None)
+    assert rc == B.MOE_EINVAL
+    rc = lib.moe_gate_up(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 48, 4, fake, None)
+    assert rc == B.MOE_EUNSUPPORTED                          # bf16 tile height must be 16/32/64/128
+    # empty batch: valid, nothing to do
+    p0 = moe.problem(0, 64, 4, 2, 64)
+    assert lib.moe_forward(ctypes.byref(p0), None, None, None, None, None, None, None, None, None, 0, None) == 0

@@ -1,0 +1,280 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer results (expert ids, counts, stable order, padded layout) must match
+bit for bit; tokens whose top-k margin in the oracle is below 1e-6 are left
+out of the id and output comparisons (and their number is printed).  Outputs:
+|gpu - ref| <= 2e-2 * max|ref| + 1e-3 in bf16, <= 1e-4 * max|ref| in fp32.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_ffn_amd as moe
+from oracle import moe_oracle as O
+from sparse_moe_ffn_amd.inputs import CONFIGS, make_inputs, random_case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+MARGIN = 1e-6
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()
+
+
+def host(t):
+    return None if t is None else t.float().cpu().numpy()
+
+
+def shared_of(h):
+    if h.get("shared_w_gate_up") is None:
+        return None
+    return {"w_gate_up": h["shared_w_gate_up"], "w_down": h["shared_w_down"], "gate": h["shared_gate"]}
+
+
+def to_host(t):
+    return {k: host(v) if isinstance(v, torch.Tensor) else v for k, v in t.items()}
+
+
+def run_forward(t, cfg):
+    return moe.moe_forward(t["x"], t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                           t["shared_w_gate_up"], t["shared_w_down"], t["shared_gate"])
+
+
+def compare_routing(h, cfg, ids_gpu, w_gpu):
+    ids_ref, w_ref, probs, margin = O.route(h["x"], h["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    keep = margin >= MARGIN
+    ids_gpu = ids_gpu.cpu().numpy()
+    w_gpu = w_gpu.cpu().numpy()
+    bad = np.nonzero((ids_gpu[keep] != ids_ref[keep]).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} routed tokens differ, first {np.nonzero(keep)[0][bad[:5]]}"
+    np.testing.assert_allclose(w_gpu[keep], w_ref[keep], rtol=2e-5, atol=2e-6)
+    return (ids_ref, w_ref, probs, margin), keep
+
+
+def check_output(out_rows, ref_rows, dtype, what=""):
+    tol = O.tolerance(ref_rows, dtype)
+    err = float(np.abs(out_rows - ref_rows).max()) if ref_rows.size else 0.0
+    assert np.isfinite(out_rows).all(), f"{what}: non-finite output"
+    assert err <= tol, f"{what}: max|gpu-ref| = {err:.4e} > tol {tol:.4e}"
+    return err, tol
+
+
+# --------------------------------------------------------------- the pages' examples
+
+def test_route_example_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "m03_route_example.json")))
+    x = torch.tensor(g["x"], dtype=torch.float32, device=DEV)
+    eye = torch.eye(g["E"], g["H"], dtype=torch.float32, device=DEV)
+    for renorm, key in ((True, "weights_renorm"), (False, "weights_no_renorm")):
+        ids, w, _ = moe.moe_route(x, eye, g["top_k"], renorm)
+        assert ids.cpu().tolist() == g["ids"]
+        assert np.round(w.cpu().double().numpy(), 4).tolist() == g[key]
+
+
+def scalar_block(g, device):
+    E = g["E"]
+    gu = torch.tensor([[[g["w_gate"][e]], [g["w_up"][e]]] for e in range(E)], dtype=torch.float32, device=device)
+    wd = torch.tensor([[[g["w_down"][e]]] for e in range(E)], dtype=torch.float32, device=device)
+    r = torch.tensor(g["router_w"], dtype=torch.float32, device=device)
+    x = torch.tensor(g["x"], dtype=torch.float32, device=device)
+    return x, r, gu, wd
+
+
+def test_scalar_block_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "m03_scalar_block.json")))
+    x, r, gu, wd = scalar_block(g, DEV)
+    ids, w, _ = moe.moe_route(x, r, g["top_k"], True)
+    assert ids.cpu().tolist() == g["ids"]
+    assert np.round(w.cpu().double().numpy(), 4).tolist() == g["weights"]
+    out = moe.moe_forward(x, r, gu, wd, g["top_k"], True)
+    assert np.round(out.cpu().double().numpy(), 4).tolist() == g["out"]
+    s = g["shared"]
+    sgu = torch.tensor(s["gate_proj"] + s["up_proj"], dtype=torch.float32, device=DEV)
+    sdn = torch.tensor(s["down_proj"], dtype=torch.float32, device=DEV)
+    sg = torch.tensor(s["gate"], dtype=torch.float32, device=DEV).reshape(-1)
+    out = moe.moe_forward(x, r, gu, wd, g["top_k"], True, sgu, sdn, sg)
+    assert np.round(out.cpu().double().numpy(), 4).tolist() == s["out_with_shared"]
+
+
+def test_align_walkthrough_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "m03_grouping_walkthrough.json")))
+    ids = torch.tensor(g["ids"], dtype=torch.int32, device=DEV)
+    gr = moe.moe_align(ids, g["E"], 2)
+    assert gr.counts.cpu().tolist() == g["counts"]
+    assert gr.order.cpu().tolist() == g["order"]
+    assert gr.offsets.cpu().tolist() == [0, 1, 2, 5, 6, 6]
+    nt = int(gr.num_tiles.item())
+    S = g["N"] * g["k"]
+    assert nt == 5
+    assert gr.sorted_pairs[:nt * 2].cpu().tolist() == [1, S, 2, S, 0, 3, 4, S, 5, S]
+    assert gr.tile_expert[:nt].cpu().tolist() == [0, 1, 2, 2, 3]
+    assert gr.tile_rows[:nt].cpu().tolist() == [1, 1, 2, 1, 1]
+
+
+# --------------------------------------------------------------- align, random ids
+
+@pytest.mark.parametrize("N,k,E,bm,dist", [
+    (3, 2, 5, 16, "uniform"), (64, 8, 128, 16, "uniform"), (4096, 8, 128, 128, "uniform"),
+    (16384, 8, 128, 128, "zipf"), (1000, 4, 7, 32, "one"), (333, 1, 1, 64, "uniform"),
+    (1, 8, 8, 16, "uniform"), (5000, 6, 512, 16, "zipf"), (777, 3, 60, 1, "uniform")])
+def test_align_matches_oracle(N, k, E, bm, dist):
+    rng = np.random.default_rng(N * 31 + E)
+    if dist == "uniform":
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(N)]) if N * k < 200000 else None
+    elif dist == "zipf":
+        wts = 1.0 / np.arange(1, E + 1) ** 1.2
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=wts / wts.sum()) for _ in range(N)])
+    else:                       # every token also picks expert 0
+        ids = np.stack([np.concatenate([[0], 1 + rng.permutation(E - 1)[:k - 1]]) for _ in range(N)])
+    gr = moe.moe_align(torch.tensor(ids, dtype=torch.int32, device=DEV), E, bm)
+    flat_e, _, _ = O.flatten_pairs(ids, np.zeros(ids.shape, np.float32))
+    order, counts, offsets = O.group_pairs(flat_e, E)
+    sp, te, tr, nt = O.pad_segments(order, counts, bm, N * k)
+    assert np.array_equal(gr.counts.cpu().numpy(), counts)
+    assert np.array_equal(gr.offsets.cpu().numpy(), offsets)
+    assert np.array_equal(gr.order.cpu().numpy(), order)
+    assert int(gr.num_tiles.item()) == nt
+    assert np.array_equal(gr.sorted_pairs[:nt * bm].cpu().numpy(), sp)
+    assert np.array_equal(gr.tile_expert[:nt].cpu().numpy(), te)
+    assert np.array_equal(gr.tile_rows[:nt].cpu().numpy(), tr)
+
+
+# --------------------------------------------------------------- whole block, small shapes
+
+SMALL = [
+    random_case(37, 64, 10, 3, 64, dtype="bf16", seed=1),
+    random_case(1, 128, 16, 4, 128, dtype="bf16", seed=2),
+    random_case(200, 128, 16, 4, 192, I_shared=128, dtype="bf16", seed=3),
+    random_case(50, 64, 6, 6, 64, dtype="bf16", seed=4),                       # k = E
+    random_case(70, 192, 9, 1, 64, dtype="bf16", seed=5, norm_topk_prob=False),  # k = 1
+    random_case(40, 64, 1, 1, 128, dtype="bf16", seed=6),                      # E = 1: a dense SwiGLU
+    random_case(300, 256, 32, 8, 128, dtype="bf16", seed=7, norm_topk_prob=False),
+    random_case(1500, 128, 8, 2, 64, dtype="bf16", seed=8),                    # block_m 128 path
+    random_case(600, 128, 16, 2, 64, dtype="bf16", seed=9),                    # block_m 64 path
+    random_case(300, 128, 16, 2, 64, dtype="bf16", seed=10),                   # block_m 32 path
+    random_case(13, 33, 5, 2, 17, I_shared=9, dtype="f32", seed=11),
+    random_case(64, 40, 12, 3, 24, dtype="f32", seed=12, norm_topk_prob=False),
+]
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS["tiny"]] + SMALL, ids=lambda c: c.name)
+def test_forward_small(cfg):
+    t = make_inputs(cfg, DEV)
+    out = run_forward(t, cfg)
+    ids_gpu, w_gpu, s_gpu = moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob, t["shared_gate"])
+    torch.cuda.synchronize()
+    h = to_host(t)
+    routing, keep = compare_routing(h, cfg, ids_gpu, w_gpu)
+    if s_gpu is not None:
+        ref_s = O.sigmoid(h["x"].astype(np.float64) @ h["shared_gate"].astype(np.float64))
+        np.testing.assert_allclose(s_gpu.cpu().numpy(), ref_s, rtol=1e-5, atol=1e-6)
+    ref, _ = O.moe_forward(h["x"], h["router_w"], h["w_gate_up"], h["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                           shared=shared_of(h), routing=routing)
+    err, tol = check_output(host(out)[keep], ref[keep], cfg.dtype, cfg.name)
+    print(f"{cfg.name}: err {err:.3e} tol {tol:.3e} excluded {int((~keep).sum())}")
+
+
+def test_empty_batch():
+    cfg = random_case(4, 64, 4, 2, 64, dtype="bf16")
+    t = make_inputs(cfg, DEV)
+    x0 = t["x"][:0]
+    out = moe.moe_forward(x0, t["router_w"], t["w_gate_up"], t["w_down"], 2, True)
+    assert out.shape == (0, 64)
+
+
+# --------------------------------------------------------------- full-size workloads
+
+_full_cache = {}
+
+
+def full_inputs(name):
+    if name not in _full_cache:
+        _full_cache.clear()
+        torch.cuda.empty_cache()
+        cfg = CONFIGS[name]
+        _full_cache[name] = (cfg, make_inputs(cfg, DEV))
+    return _full_cache[name]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "talker"])
+def test_full_size_parity(name):
+    cfg, t = full_inputs(name)
+    out = run_forward(t, cfg)
+    out2 = run_forward(t, cfg)
+    ids_gpu, w_gpu, _ = moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob, None)
+    lay = moe.moe_get_workspace_layout(moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], cfg.top_k,
+                                                        cfg.norm_topk_prob, t["shared_w_gate_up"]))
+    gr = moe.moe_align(ids_gpu, cfg.E, lay["block_m"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "two runs differ"
+    h = {"x": host(t["x"]), "router_w": host(t["router_w"])}
+    routing, keep = compare_routing(h, cfg, ids_gpu, w_gpu)
+    ids_ref = routing[0]
+    # grouping: exact, with the excluded tokens' pairs removed on both sides
+    k = cfg.top_k
+    excluded = np.nonzero(~keep)[0]
+    ids_g = ids_gpu.cpu().numpy()
+    counts_g = gr.counts.cpu().numpy().astype(np.int64)
+    flat_ref, _, _ = O.flatten_pairs(ids_ref, routing[1])
+    order_r, counts_r, _ = O.group_pairs(flat_ref, cfg.E)
+    for n in excluded:
+        for j in range(k):
+            counts_g[ids_g[n, j]] -= 1
+            counts_r[ids_ref[n, j]] -= 1
+    assert np.array_equal(counts_g, counts_r)
+    drop = np.zeros(cfg.N * k, bool)
+    for n in excluded:
+        drop[n * k:(n + 1) * k] = True
+    order_g = gr.order.cpu().numpy()
+    assert np.array_equal(order_g[~drop[order_g]], order_r[~drop[order_r]])
+    # outputs on sampled tokens
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, cfg.N - 1] + rng.choice(cfg.N, size=min(cfg.N, 22), replace=False).tolist()))
+    rows = [r for r in rows if keep[r]]
+    hw = {"w_gate_up": host(t["w_gate_up"]), "w_down": host(t["w_down"])}
+    sh = None
+    if cfg.I_shared:
+        sh = {"w_gate_up": host(t["shared_w_gate_up"]), "w_down": host(t["shared_w_down"]),
+              "gate": host(t["shared_gate"])}
+    ref, _ = O.moe_forward(h["x"], h["router_w"], hw["w_gate_up"], hw["w_down"], k, cfg.norm_topk_prob,
+                           shared=sh, rows=rows, routing=routing)
+    err, tol = check_output(host(out)[rows], ref, cfg.dtype, name)
+    nz = int((counts_r == 0).sum())
+    print(f"{name}: err {err:.3e} tol {tol:.3e} excluded tokens {excluded.size} "
+          f"counts min/max {counts_r.min()}/{counts_r.max()} empty experts {nz}")
+    if cfg.skew:
+        assert nz >= cfg.skew_dead
+
+
+@pytest.mark.slow
+def test_batch_invariance_decode_layer():
+    cfg, t = full_inputs("decode")
+    full = run_forward(t, cfg)
+    for i in (0, 17, 63):
+        one = moe.moe_forward(t["x"][i:i + 1].contiguous(), t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k,
+                              cfg.norm_topk_prob)
+        assert torch.equal(one[0], full[i]), f"token {i}"
+
+
+@pytest.mark.slow
+def test_staged_calls_equal_forward():
+    cfg, t = full_inputs("decode")
+    out = run_forward(t, cfg)
+    lay = moe.moe_get_workspace_layout(moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], cfg.top_k,
+                                                        cfg.norm_topk_prob))
+    ids, w, _ = moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    gr = moe.moe_align(ids, cfg.E, lay["block_m"])
+    act = moe.moe_gate_up(t["x"], t["w_gate_up"], gr, cfg.top_k)
+    y = moe.moe_down(act, t["w_down"], w, gr, cfg.N, cfg.top_k)
+    out2 = moe.moe_combine(y, cfg.N, cfg.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)

@@ -278,6 +278,9 @@ def test_scalar_block_pin_catches_assignment(monkeypatch):
         def __call__(self, *a, **k):
             return np.add(*a, **k)
 
+        def __getattr__(self, name):
+            return getattr(np.add, name)
+
     fake = _NP()
     fake.add = _Add()
     monkeypatch.setattr(O, "np", fake)
