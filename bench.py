@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE FFN block on one MI355X.
+
+One step = one full pass of the block (router, align, gate/up, down,
+[shared expert], combine) over one batch of seeded synthetic tokens already
+resident in HBM, through the C ABI (``moe_forward``).
+
+Prints ONE JSON line.  ``value`` is tokens/s of the main workload (default:
+the 64-token decode layer, H=2048, E=128, top-8, I=768, bf16).  ``roofline``
+is for the dominant kernel of that workload, timed with HIP events on the
+stream the kernels run on, in a second loop that issues the same stages one
+by one.  ``cpu_baseline`` times the CPU oracle on a bounded token sample.
+``also`` holds the same figures for the other workloads given with --also.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+METRIC = "MoE-layer tokens/s; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "talker"])
+    ap.add_argument("--also", default="prefill", help="comma-separated extra workloads ('' for none)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def expert_hits(counts):
+    return int((counts > 0).sum())
+
+
+def kernel_work(cfg, counts):
+    """Algorithmic bytes and flops per launch of each kernel.
+
+    gate_up: weights of every hit expert (2I x H) once, each token's x row
+    once, and one act row (I) per pair; flops 2*H*2I per pair.
+    down: weights of every hit expert (H x I) once, one act row in and one y
+    row (H) out per pair; flops 2*I*H per pair.
+    """
+    es = 2 if cfg.dtype == "bf16" else 4
+    P = cfg.N * cfg.top_k
+    hit = expert_hits(counts)
+    gu_bytes = hit * 2 * cfg.I * cfg.H * es + cfg.N * cfg.H * es + P * cfg.I * es
+    dn_bytes = hit * cfg.H * cfg.I * es + P * cfg.I * es + P * cfg.H * es
+    return {
+        "gate_up": {"bytes": gu_bytes, "flops": 2.0 * P * cfg.H * 2 * cfg.I},
+        "down": {"bytes": dn_bytes, "flops": 2.0 * P * cfg.I * cfg.H},
+    }
+
+
+def bench_workload(name, steps, warmup, torch, moe):
+    from sparse_moe_ffn_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[name]
+    dev = torch.device("cuda:0")
+    t = make_inputs(cfg, dev)
+    args = (t["x"], t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
+            t["shared_w_gate_up"], t["shared_w_down"], t["shared_gate"])
+    p = moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], cfg.top_k, cfg.norm_topk_prob,
+                         t["shared_w_gate_up"])
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(t["x"])
+    for _ in range(warmup):
+        moe.moe_forward(*args, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        moe.moe_forward(*args, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # Same stages issued one by one, HIP events between them, on the stream
+    # the kernels run on (torch's current stream).
+    lay = moe.moe_get_workspace_layout(p)
+    bm = lay["block_m"]
+    stages = ["route", "align", "gate_up", "down"] + (["shared"] if cfg.I_shared else []) + ["combine"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    ids = torch.empty((cfg.N, cfg.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((cfg.N, cfg.top_k), dtype=torch.float32, device=dev)
+    sscale = torch.empty(cfg.N, dtype=torch.float32, device=dev) if cfg.I_shared else None
+    gr = moe.moe_align(ids.zero_(), cfg.E, bm)
+    act = torch.empty((gr.max_rows, cfg.I), dtype=t["x"].dtype, device=dev)
+    y = torch.empty((cfg.N * cfg.top_k, cfg.H), dtype=t["x"].dtype, device=dev)
+    sact = torch.empty((cfg.N, cfg.I_shared), dtype=t["x"].dtype, device=dev) if cfg.I_shared else None
+    sy = torch.empty((cfg.N, cfg.H), dtype=t["x"].dtype, device=dev) if cfg.I_shared else None
+
+    def staged(e):
+        e[0].record()
+        moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob, t["shared_gate"], ids, wts, sscale)
+        e[1].record()
+        g2 = moe.moe_align(ids, cfg.E, bm)
+        e[2].record()
+        moe.moe_gate_up(t["x"], t["w_gate_up"], g2, cfg.top_k, act)
+        e[3].record()
+        moe.moe_down(act, t["w_down"], wts, g2, cfg.N, cfg.top_k, y)
+        e[4].record()
+        i = 5
+        if cfg.I_shared:
+            moe.moe_shared_expert(t["x"], t["shared_w_gate_up"], t["shared_w_down"], sscale, sact, sy)
+            e[i].record()
+            i += 1
+        moe.moe_combine(y, cfg.N, cfg.top_k, sy, out)
+        e[i].record()
+        return g2
+
+    for _ in range(min(warmup, 5)):
+        g2 = staged(ev[0])
+    torch.cuda.synchronize()
+    for s in range(steps):
+        g2 = staged(ev[s])
+    torch.cuda.synchronize()
+    stage_ms = {name_: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+                for i, name_ in enumerate(stages)}
+    counts = g2.counts.cpu().numpy()
+    work = kernel_work(cfg, counts)
+    ms = elapsed / steps * 1e3
+    res = {
+        "cfg": cfg, "inputs": t, "ms_per_step": ms, "tokens_per_s": cfg.N / (ms * 1e-3),
+        "tflops": cfg.flops() / (ms * 1e-3) / 1e12, "stage_ms": stage_ms, "work": work,
+        "hit_experts": expert_hits(counts), "counts_min_max": [int(counts.min()), int(counts.max())],
+    }
+    res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFLOPS
+    weight_bytes = res["hit_experts"] * 3 * cfg.I * cfg.H * 2 + cfg.I_shared * 3 * cfg.H * 2
+    res["weight_hbm_frac"] = weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    return res
+
+
+def roofline_for(res):
+    cfg = res["cfg"]
+    kern = "gate_up"
+    dur_s = res["stage_ms"][kern] * 1e-3
+    w = res["work"][kern]
+    if cfg.N * cfg.top_k / cfg.E < 64:          # few rows per expert: a weight stream
+        achieved = w["bytes"] / dur_s / 1e9
+        return {"kernel": "grouped_gemm_bf16 gate_up (SwiGLU epilogue)", "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": w["bytes"], "avg_launch_ms": round(res["stage_ms"][kern], 4)}
+    achieved = w["flops"] / dur_s / 1e12
+    return {"kernel": "grouped_gemm_bf16 gate_up (SwiGLU epilogue)", "bound": "mfma", "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None, "algorithmic_flops_per_launch": w["flops"], "avg_launch_ms": round(res["stage_ms"][kern], 4)}
+
+
+def cpu_baseline(res, budget_s, torch):
+    """The CPU oracle, as it is, on the first tokens of the same workload
+    until the time budget is spent (routing of the whole batch included)."""
+    import numpy as np
+    from oracle import moe_oracle as O
+
+    cfg, t = res["cfg"], res["inputs"]
+    h = {k: (v.float().cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    sh = None
+    if cfg.I_shared:
+        sh = {"w_gate_up": h["shared_w_gate_up"], "w_down": h["shared_w_down"], "gate": h["shared_gate"]}
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    routing = O.route(h["x"], h["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    done = 0
+    while done < cfg.N and (time.perf_counter() - t0) < budget_s:
+        O.moe_forward(h["x"], h["router_w"], h["w_gate_up"], h["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                      shared=sh, rows=[done], routing=routing)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {done} of {cfg.N} tokens of the {cfg.name} layer (routing of all {cfg.N}), "
+                      f"{el:.1f} s, numpy float64 expert math"}
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return n
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (the block has no multi-GPU path).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_moe_ffn_amd as moe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.load_library()
+    print(f"[bench] workload {a.workload}: {a.warmup} warmup + {a.steps} timed steps", file=sys.stderr, flush=True)
+    main_res = bench_workload(a.workload, a.steps, a.warmup, torch, moe)
+    also = {}
+    for w in [s for s in a.also.split(",") if s and s != a.workload]:
+        print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+        r = bench_workload(w, max(10, a.steps // 10), max(3, a.warmup // 4), torch, moe)
+        also[w] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                   "tflops": round(r["tflops"], 1), "mfma_frac": round(r["mfma_frac"], 4),
+                   "weight_hbm_frac": round(r["weight_hbm_frac"], 4),
+                   "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+                   "roofline": roofline_for(r), "counts_min_max": r["counts_min_max"]}
+        del r
+        torch.cuda.empty_cache()
+    if a.copy_calibration:
+        copy_calibration(torch)
+    cpu = None
+    if a.cpu_seconds > 0:
+        print("[bench] cpu oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(main_res, a.cpu_seconds, torch)
+    cfg = main_res["cfg"]
+    line = {
+        "metric": METRIC, "value": round(main_res["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Qwen3-30B-A3B-shaped MoE layer", "tokens": cfg.N, "hidden": cfg.H,
+                   "experts": cfg.E, "top_k": cfg.top_k, "inter": cfg.I, "shared_inter": cfg.I_shared,
+                   "norm_topk_prob": cfg.norm_topk_prob, "seed": cfg.seed},
+        "tflops": round(main_res["tflops"], 2), "mfma_frac": round(main_res["mfma_frac"], 4),
+        "weight_hbm_frac": round(main_res["weight_hbm_frac"], 4),
+        "stage_ms": {k: round(v, 4) for k, v in main_res["stage_ms"].items()},
+        "hit_experts": main_res["hit_experts"],
+        "roofline": roofline_for(main_res), "cpu_baseline": cpu, "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

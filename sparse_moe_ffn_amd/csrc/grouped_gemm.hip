@@ -34,33 +34,65 @@
 
 namespace moe {
 
-constexpr int kBK = 64;          // K elements per stage (128 bytes of bf16)
-constexpr int kChunksPerRow = kBK / 8;
+constexpr int kBK = 64;                 // K elements per stage: 128-byte bf16 rows
+constexpr int kRowsPerDma = 8;          // one wave-wide 16-byte-per-lane DMA fills 8 rows
 
 enum { kGateUp = 0, kDown = 1 };
 
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_u16_t*)p));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes lds_base + 16*i (lds_base wave-uniform, in M0).  Issued as inline
+// assembly so that the compiler does not serialise the pipeline with its own
+// conservative waits on LDS DMA; completion is tracked by hand with vmcnt
+// (vector-memory loads complete in issue order).
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left unconstrained).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Element offset of 16-byte chunk `chunk` of row `row` in a staged tile: the
+// chunk index is XOR-ed with the row's low bits so that 16 lanes reading one
+// chunk column of 16 consecutive rows spread over the banks.
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kBK + ((chunk ^ (row & 7)) << 3);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
-  constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M;
   constexpr int WN = BN / WAVES_N;
   constexpr int TM = WM / 16;
   constexpr int TN = WN / 16;
+  constexpr int ROWS = BM + BN;                     // staged rows: A tile, then B tile
+  constexpr int NDMA = ROWS / kRowsPerDma;          // wave DMAs per stage
+  constexpr int PER_WAVE = NDMA / NW;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(MODE != kGateUp || TN % 2 == 0, "gate/up needs matching gate and up sub-tiles");
-  constexpr int kAChunks = BM * kChunksPerRow;
-  constexpr int kBChunks = BN * kChunksPerRow;
-  constexpr int kALoads = (kAChunks + kThreads - 1) / kThreads;
-  constexpr int kBLoads = (kBChunks + kThreads - 1) / kThreads;
+  static_assert(NDMA % NW == 0, "stage rows must split evenly over the waves");
+  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][(BM + BN) * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES][ROWS * kBK];
 
   const bool grouped = g.sorted_pairs != nullptr;
-  const int n_tiles_n = (MODE == kGateUp) ? g.n_out / (BN / 2) : (g.n_out + BN - 1) / BN;
+  const int half = BN / 2;
+  const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + half - 1) / half : (g.n_out + BN - 1) / BN;
   const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   const int mt = logical % g.max_tiles;
   const int nt = logical / g.max_tiles;
@@ -77,54 +109,66 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   }
   const int row0 = mt * BM;
   const int K = g.K;
-  const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
   const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.a);
-  const uint16_t* __restrict__ B =
-      static_cast<const uint16_t*>(g.b) + (int64_t)expert * g.expert_stride;
+  const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.b) + (int64_t)expert * g.expert_stride;
+  const int64_t b_rows = (MODE == kGateUp) ? 2 * (int64_t)g.n_out : g.n_out;
 
-  // Per-thread global sources of its A and B chunks (fixed over K).
-  const uint16_t* a_src[kALoads];
-  int a_dst[kALoads];
+  // Sources of this lane's 16-byte pieces: DMA q of this wave fills staged
+  // rows [8*gi, 8*gi + 8) with gi = wave + NW*q; lane i lands in row
+  // 8*gi + i/8, slot i%8, which holds chunk (i%8) ^ (row & 7).
+  const uint16_t* src[PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < kALoads; ++i) {
-    const int c = tid + i * kThreads;
-    const int r = c / kChunksPerRow, ch = c % kChunksPerRow;
-    a_dst[i] = (c < kAChunks) ? swz(r, ch) : -1;
-    int64_t src_row;
-    if (MODE == kGateUp) {
-      if (grouped) {
-        const int pr = (c < kAChunks) ? g.sorted_pairs[row0 + r] : g.num_pairs;
-        src_row = (pr < g.num_pairs) ? pr / g.top_k : 0;       // sentinel rows read token 0
+  for (int q = 0; q < PER_WAVE; ++q) {
+    const int gi = wave + NW * q;
+    const int r = gi * kRowsPerDma + (lane >> 3);
+    const int chunk = (lane & 7) ^ (r & 7);
+    const uint16_t* row_ptr;
+    if (r < BM) {
+      int64_t src_row;
+      if (MODE == kGateUp) {
+        if (grouped) {
+          const int pr = g.sorted_pairs[row0 + r];
+          src_row = (pr < g.num_pairs) ? pr / g.top_k : 0;     // sentinel rows read token 0
+        } else {
+          src_row = min(row0 + r, g.dense_rows - 1);
+        }
       } else {
-        src_row = min(row0 + r, g.dense_rows - 1);
+        src_row = grouped ? (row0 + r) : min(row0 + r, g.dense_rows - 1);
       }
+      row_ptr = A + src_row * K;
     } else {
-      src_row = grouped ? (row0 + r) : min(row0 + r, g.dense_rows - 1);
+      const int j = r - BM;
+      int64_t wrow;
+      if (MODE == kGateUp)
+        wrow = (j < half) ? (int64_t)nt * half + j : (int64_t)g.n_out + nt * half + (j - half);
+      else
+        wrow = (int64_t)nt * BN + j;
+      if (MODE == kGateUp) {                         // past the last column: reread a valid row
+        const int64_t lim = (j < half) ? g.n_out - 1 : b_rows - 1;
+        wrow = min(wrow, lim);
+      } else {
+        wrow = min(wrow, b_rows - 1);
+      }
+      row_ptr = B + wrow * K;
     }
-    a_src[i] = A + src_row * K + ch * 8;
+    src[q] = row_ptr + chunk * 8;
   }
-  const uint16_t* b_src[kBLoads];
-  int b_dst[kBLoads];
+
+  auto issue = [&](int kt, int st) {
 #pragma unroll
-  for (int i = 0; i < kBLoads; ++i) {
-    const int c = tid + i * kThreads;
-    const int j = c / kChunksPerRow, ch = c % kChunksPerRow;
-    b_dst[i] = (c < kBChunks) ? swz(j, ch) : -1;
-    int64_t wrow;
-    if (MODE == kGateUp) {
-      const int half = BN / 2;
-      wrow = (j < half) ? (int64_t)nt * half + j : (int64_t)g.n_out + nt * half + (j - half);
-    } else {
-      wrow = (int64_t)nt * BN + j;
-      if (wrow >= g.n_out) b_dst[i] = -2 - b_dst[i];           // outside: store zeros
-    }
-    b_src[i] = B + min(wrow, (int64_t)(MODE == kGateUp ? 2 * g.n_out : g.n_out) - 1) * K + ch * 8;
-  }
+    for (int q = 0; q < PER_WAVE; ++q)
+      dma16(src[q] + kt * kBK, lds_addr(&smem[st][(wave + NW * q) * kRowsPerDma * kBK]));
+  };
+  auto wait_stage = [&](int ahead) {                 // ahead: stages issued past the current one
+    if (STAGES >= 4 && ahead >= 2) wait_vmcnt<((STAGES >= 4) ? 2 : 0) * PER_WAVE>();
+    else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<((STAGES >= 3) ? 1 : 0) * PER_WAVE>();
+    else wait_vmcnt<0>();
+  };
 
   floatx4 acc[TM][TN];
 #pragma unroll
@@ -132,71 +176,52 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[kALoads], rb[kBLoads];
-  auto load_stage = [&](int kt) {
-    const int koff = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < kALoads; ++i)
-      if (a_dst[i] >= 0) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + koff);
-#pragma unroll
-    for (int i = 0; i < kBLoads; ++i)
-      if (b_dst[i] >= 0) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + koff);
-  };
-  auto store_stage = [&](int st) {
-    uint16_t* As = smem[st];
-    uint16_t* Bs = smem[st] + BM * kBK;
-#pragma unroll
-    for (int i = 0; i < kALoads; ++i)
-      if (a_dst[i] >= 0) *reinterpret_cast<uint4*>(As + a_dst[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < kBLoads; ++i) {
-      if (b_dst[i] >= 0) *reinterpret_cast<uint4*>(Bs + b_dst[i]) = rb[i];
-      else if (b_dst[i] <= -2) *reinterpret_cast<uint4*>(Bs + (-2 - b_dst[i])) = uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  // Row of the B tile read by sub-tile tn of this wave.
+  // 16-row sub-tiles of this wave that hold real rows (the rest is padding).
+  const int tm_valid = min(TM, max(0, (rows_valid - wm * WM + 15) / 16));
+
   auto b_tile_row = [&](int tn) {
     if (MODE == kGateUp) {
       constexpr int kHalfTN = TN / 2;
       const int part = tn / kHalfTN, t = tn % kHalfTN;
-      return part * (BN / 2) + wn * (WN / 2) + t * 16 + (lane & 15);
+      return part * half + wn * (WN / 2) + t * 16 + (lane & 15);
     }
     return wn * WN + tn * 16 + (lane & 15);
   };
 
   const int nk = K / kBK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s, s);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_stage(kt + 1);
-    const uint16_t* As = smem[kt & 1];
-    const uint16_t* Bs = smem[kt & 1] + BM * kBK;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 32; ++kk) {
-      const int ch = kk * 4 + (lane >> 4);
-      uint4 af[TM], bfr[TN];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int r = wm * WM + tm * 16 + (lane & 15);
-        af[tm] = *reinterpret_cast<const uint4*>(As + swz(r, ch));
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz(b_tile_row(tn), ch));
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(af[tm], bfr[tn], acc[tm][tn]);
-    }
-    if (kt + 1 < nk) store_stage((kt + 1) & 1);
+    wait_stage(min(nk - 1 - kt, STAGES - 2));
     __syncthreads();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    if (tm_valid > 0) {                              // waves holding only padding rows skip
+      const uint16_t* As = smem[kt % STAGES];
+      const uint16_t* Bs = As + BM * kBK;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 32; ++kk) {
+        const int ch = kk * 4 + (lane >> 4);
+        uint4 af[TM], bfr[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+          bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz(b_tile_row(tn), ch));
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+          af[tm] = *reinterpret_cast<const uint4*>(As + swz(wm * WM + tm * 16 + (lane & 15), ch));
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(af[tm], bfr[tn], acc[tm][tn]);
+      }
+    }
   }
 
   // Epilogue: lane holds rows 4*(lane/16)+i of column lane%16 of each sub-tile.
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
+    if (tm >= tm_valid) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * WM + tm * 16 + (lane >> 4) * 4 + i;
@@ -206,9 +231,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
         uint16_t* out_row = C + (int64_t)(row0 + r) * g.n_out;
 #pragma unroll
         for (int t = 0; t < kHalfTN; ++t) {
-          const int col = nt * (BN / 2) + wn * (WN / 2) + t * 16 + (lane & 15);
-          const float gv = acc[tm][t][i], uv = acc[tm][t + kHalfTN][i];
-          out_row[col] = f32_to_bf16(silu_f32(gv) * uv);
+          const int col = nt * half + wn * (WN / 2) + t * 16 + (lane & 15);
+          if (col < g.n_out) {
+            const float gv = acc[tm][t][i], uv = acc[tm][t + kHalfTN][i];
+            out_row[col] = f32_to_bf16(silu_f32(gv) * uv);
+          }
         }
       } else {
         const int prow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
@@ -276,13 +303,13 @@ __global__ __launch_bounds__(kF32Threads) void grouped_gemm_f32_kernel(GemmProbl
 
 // ---------------------------------------------------------------- launchers
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int MODE>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE>
 static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
-  const int n_tiles_n = (MODE == kGateUp) ? g.n_out / (BN / 2) : (g.n_out + BN - 1) / BN;
+  const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
   const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, MODE>), dim3((unsigned)blocks),
-                     dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, MODE>),
+                     dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
   return hipGetLastError();
 }
 
@@ -295,10 +322,10 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     return hipGetLastError();
   }
   switch (g.block_m) {
-    case 16: return launch_bf16<16, 128, 1, 4, MODE>(g, s);
-    case 32: return launch_bf16<32, 128, 1, 4, MODE>(g, s);
-    case 64: return launch_bf16<64, 128, 2, 2, MODE>(g, s);
-    case 128: return launch_bf16<128, 128, 2, 2, MODE>(g, s);
+    case 16: return launch_bf16<16, 128, 1, 2, 4, MODE>(g, s);
+    case 32: return launch_bf16<32, 128, 1, 4, 4, MODE>(g, s);
+    case 64: return launch_bf16<64, 256, 1, 4, 3, MODE>(g, s);
+    case 128: return launch_bf16<128, 256, 2, 2, 3, MODE>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

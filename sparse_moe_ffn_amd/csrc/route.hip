@@ -8,11 +8,10 @@
 // Qwen3MoeSparseMoeBlock forward.
 //
 // One workgroup routes 16 tokens.  bf16: the [16 x (E+1)] logit tile is a
-// matrix-core product (16x16x32 bf16 MFMA, float32 accumulation) with the
-// expert columns spread over 4 waves; fp32: plain FMA dot products.  The
-// tile goes to LDS, then each wave routes 4 tokens: two probabilities per
-// lane for E = 128, wave-wide max / sum, and k rounds of a (value, id)
-// wave argmax.
+// matrix-core product (16x16x32 bf16 MFMA, float32 accumulation) with H split
+// over 8 waves; fp32: plain FMA dot products.  The tile goes to LDS, then
+// each wave routes its tokens: two probabilities per lane for E = 128,
+// wave-wide max / sum, and k rounds of a (value, id) wave argmax.
 #include <float.h>
 #include <limits.h>
 
@@ -25,9 +24,10 @@ constexpr int kRouteTok = 16;
 constexpr int kRouteThreads = 256;
 constexpr int kRouteWaves = kRouteThreads / kWave;
 constexpr int kRouteMaxCols = ((kMaxExperts + 1 + 15) / 16) * 16;            // 528
-constexpr int kRouteMaxSub = (kRouteMaxCols / 16 + kRouteWaves - 1) / kRouteWaves;  // 9
 constexpr int kRoutePer = kMaxExperts / kWave;                                 // 8
 constexpr int kLogitLd = kRouteMaxCols + 1;
+constexpr int kRouteBf16Waves = 8;
+constexpr int kRouteBf16Threads = kRouteBf16Waves * kWave;
 
 // Softmax, top-k and renormalisation of one token, by one whole wave.
 __device__ void route_token(const float* __restrict__ logit, int E, int k, int norm,
@@ -93,7 +93,8 @@ __device__ void route_token(const float* __restrict__ logit, int E, int k, int n
 __device__ void route_tile_from_lds(const float (*logits)[kLogitLd], int t0, int N, int E, int k, int norm,
                                     int has_shared, int32_t* ids, float* w, float* shared_scale) {
   const int wave = threadIdx.x / kWave;
-  for (int t = wave; t < kRouteTok; t += kRouteWaves) {
+  const int nwaves = blockDim.x / kWave;
+  for (int t = wave; t < kRouteTok; t += nwaves) {
     const int n = t0 + t;
     if (n >= N) break;
     route_token(logits[t], E, k, norm, ids + (int64_t)n * k, w + (int64_t)n * k);
@@ -101,7 +102,14 @@ __device__ void route_tile_from_lds(const float (*logits)[kLogitLd], int t0, int
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
+// bf16 logits: the 16 x (E [+1]) tile is a matrix-core product, computed in
+// groups of up to 144 columns.  The K dimension is dealt round-robin to the
+// 8 waves (32 columns of H per step), every wave covers all columns of the
+// group, and the 8 partial tiles are summed through LDS in wave order, so
+// each logit is reduced in a fixed order that does not depend on the batch.
+constexpr int kRouteSub = 9;                 // 16-column sub-tiles per group
+
+__global__ __launch_bounds__(kRouteBf16Threads) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ router_w,
     const uint16_t* __restrict__ shared_gate, int N, int H, int E, int k, int norm,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ shared_scale) {
@@ -112,43 +120,49 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(
   const int cols = E + (shared_gate ? 1 : 0);
   const int nsub = (cols + 15) / 16;
 
-  // A fragment source: token row lane%16 (clamped), k-block lane/16.
   const int arow = min(t0 + (lane & 15), N - 1);
   const uint16_t* a_src = x + (int64_t)arow * H + (lane >> 4) * 8;
-
-  const uint16_t* b_src[kRouteMaxSub];
-  floatx4 acc[kRouteMaxSub];
-#pragma unroll
-  for (int i = 0; i < kRouteMaxSub; ++i) {
-    const int sub = wave + kRouteWaves * i;
-    const int c = sub * 16 + (lane & 15);
-    const uint16_t* src = nullptr;
-    if (c < E) src = router_w + (int64_t)c * H;
-    else if (c == E && shared_gate) src = shared_gate;
-    b_src[i] = src ? src + (lane >> 4) * 8 : nullptr;
-    acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
   const uint4 zero = {0u, 0u, 0u, 0u};
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    const uint4 a = *reinterpret_cast<const uint4*>(a_src + k0);
+  for (int s0 = 0; s0 < nsub; s0 += kRouteSub) {
+    const int gsub = min(kRouteSub, nsub - s0);
+    const uint16_t* b_src[kRouteSub];
+    floatx4 acc[kRouteSub];
 #pragma unroll
-    for (int i = 0; i < kRouteMaxSub; ++i) {
-      if (wave + kRouteWaves * i < nsub) {                 // wave-uniform
-        const uint4 b = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
-        acc[i] = mfma16x16x32(a, b, acc[i]);
+    for (int i = 0; i < kRouteSub; ++i) {
+      const int c = (s0 + i) * 16 + (lane & 15);
+      const uint16_t* src = nullptr;
+      if (c < E) src = router_w + (int64_t)c * H;
+      else if (c == E && shared_gate) src = shared_gate;
+      b_src[i] = src ? src + (lane >> 4) * 8 : nullptr;
+      acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int k0 = wave * 32; k0 < H; k0 += kRouteBf16Waves * 32) {
+      const uint4 a = *reinterpret_cast<const uint4*>(a_src + k0);
+      uint4 b[kRouteSub];
+#pragma unroll
+      for (int i = 0; i < kRouteSub; ++i)
+        if (i < gsub) b[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
+#pragma unroll
+      for (int i = 0; i < kRouteSub; ++i)
+        if (i < gsub) acc[i] = mfma16x16x32(a, b[i], acc[i]);
+    }
+    for (int wv = 0; wv < kRouteBf16Waves; ++wv) {
+      if (wave == wv) {
+#pragma unroll
+        for (int i = 0; i < kRouteSub; ++i) {
+          if (i < gsub) {
+            const int c = (s0 + i) * 16 + (lane & 15);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float& dst = logits[(lane >> 4) * 4 + r][c];
+              dst = (wv == 0) ? acc[i][r] : dst + acc[i][r];
+            }
+          }
+        }
       }
+      __syncthreads();
     }
   }
-#pragma unroll
-  for (int i = 0; i < kRouteMaxSub; ++i) {
-    const int sub = wave + kRouteWaves * i;
-    if (sub < nsub) {
-      const int c = sub * 16 + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) logits[(lane >> 4) * 4 + r][c] = acc[i][r];
-    }
-  }
-  __syncthreads();
   route_tile_from_lds(logits, t0, N, E, k, norm, shared_gate != nullptr, ids, w, shared_scale);
 }
 
@@ -178,7 +192,7 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* router_
   const int N = (int)p.num_tokens, H = (int)p.hidden, E = (int)p.num_experts, k = (int)p.top_k;
   const dim3 grid((N + kRouteTok - 1) / kRouteTok);
   if (p.dtype == MOE_BF16) {
-    hipLaunchKernelGGL(route_bf16_kernel, grid, dim3(kRouteThreads), 0, s,
+    hipLaunchKernelGGL(route_bf16_kernel, grid, dim3(kRouteBf16Threads), 0, s,
                        (const uint16_t*)x, (const uint16_t*)router_w, (const uint16_t*)shared_gate,
                        N, H, E, k, (int)p.norm_topk_prob, ids, w, shared_scale);
   } else {
