@@ -17,9 +17,9 @@
 // host never reads the count.
 //
 // bf16 kernel (gfx950): C = A . B^T with A gathered rows [BM, K] and B the
-// expert's weight rows [BN, K], both K-contiguous.  64-wide K steps are
-// staged through LDS, double buffered (global loads of step s+1 in flight
-// while the matrix cores work on step s), 128-byte rows with their 16-byte
+// expert's weight rows [BN, K], both K-contiguous.  64-wide K steps go from
+// global memory straight into LDS (16-byte-per-lane DMA), 2-3 steps ahead of
+// the matrix cores, one barrier per step; 128-byte rows with their 16-byte
 // chunks XOR-swizzled by row so fragment reads hit distinct banks.  Each wave
 // owns a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 16x16x32 bf16 MFMAs with
 // float32 accumulators.  For gate/up a B tile holds BN/2 gate rows and the
@@ -29,6 +29,8 @@
 // they meet the same weight tile in that XCD's L2.
 //
 // fp32 kernel: plain FMA loops, any shape (used for float32 layers).
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -93,18 +95,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   const bool grouped = g.sorted_pairs != nullptr;
   const int half = BN / 2;
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + half - 1) / half : (g.n_out + BN - 1) / BN;
-  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int mt = logical % g.max_tiles;
-  const int nt = logical / g.max_tiles;
-  if (nt >= n_tiles_n) return;
+  // Workgroups past the real number of tiles leave at once; the others are
+  // ordered column-block-fastest and chunked per XCD, so one XCD runs all
+  // column blocks of a few consecutive row tiles together: they share the
+  // gathered A rows and (row tiles of one expert) the expert's weights in
+  // that XCD's L2.
+  const int m_tiles = grouped ? *g.num_tiles : (g.dense_rows + BM - 1) / BM;
+  const int n_blocks = m_tiles * n_tiles_n;
+  if ((int)blockIdx.x >= n_blocks) return;
+  const int logical = xcd_swizzle(blockIdx.x, n_blocks);
+  const int mt = logical / n_tiles_n;
+  const int nt = logical % n_tiles_n;
   int rows_valid, expert;
   if (grouped) {
-    if (mt >= *g.num_tiles) return;
     rows_valid = g.tile_rows[mt];
     expert = g.tile_expert[mt];
   } else {
     rows_valid = min(BM, g.dense_rows - mt * BM);
-    if (rows_valid <= 0) return;
     expert = 0;
   }
   const int row0 = mt * BM;
@@ -188,66 +195,99 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
     return wn * WN + tn * 16 + (lane & 15);
   };
 
+  // The K loop.  Waves that hold only padding rows still issue their share
+  // of the DMAs and take part in every barrier, but run a copy of the loop
+  // without matrix work (choosing the copy outside the loop keeps both
+  // bodies branch-free, so the accumulators stay in AGPRs).
   const int nk = K / kBK;
+  auto main_loop = [&](auto compute) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_stage(min(nk - 1 - kt, STAGES - 2));
-    __syncthreads();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    if (tm_valid > 0) {                              // waves holding only padding rows skip
-      const uint16_t* As = smem[kt % STAGES];
-      const uint16_t* Bs = As + BM * kBK;
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s, s);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_stage(min(nk - 1 - kt, STAGES - 2));
+      __syncthreads();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      if constexpr (decltype(compute)::value) {
+        const uint16_t* As = smem[kt % STAGES];
+        const uint16_t* Bs = As + BM * kBK;
 #pragma unroll
-      for (int kk = 0; kk < kBK / 32; ++kk) {
-        const int ch = kk * 4 + (lane >> 4);
-        uint4 af[TM], bfr[TN];
+        for (int kk = 0; kk < kBK / 32; ++kk) {
+          const int ch = kk * 4 + (lane >> 4);
+          uint4 af[TM], bfr[TN];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz(b_tile_row(tn), ch));
+          for (int tn = 0; tn < TN; ++tn)
+            bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz(b_tile_row(tn), ch));
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-          af[tm] = *reinterpret_cast<const uint4*>(As + swz(wm * WM + tm * 16 + (lane & 15), ch));
+          for (int tm = 0; tm < TM; ++tm)
+            af[tm] = *reinterpret_cast<const uint4*>(As + swz(wm * WM + tm * 16 + (lane & 15), ch));
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
+          for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
-          for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(af[tm], bfr[tn], acc[tm][tn]);
+            for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(bfr[tn], af[tm], acc[tm][tn]);
+        }
+      }
+    }
+  };
+  if (tm_valid > 0)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
+
+  // Epilogue.  The products were taken with the weight fragment as the MFMA's
+  // row operand, so lane l holds output columns 4*(l/16) .. +3 of row l%16 of
+  // each 16x16 sub-tile.  The tile is finished in registers (SwiGLU, or the
+  // routing weight), packed to bf16 four columns at a time into LDS (the
+  // pipeline buffers are free now), then written out as whole rows with
+  // 16-byte stores.
+  constexpr int OUT_COLS = (MODE == kGateUp) ? BN / 2 : BN;
+  constexpr int OUT_LD = OUT_COLS + 8;                 // staged row pitch (+16 B against bank conflicts)
+  static_assert(BM * OUT_LD * 2 <= (int)sizeof(smem), "output tile must fit the LDS");
+  uint16_t* so = &smem[0][0];
+  __syncthreads();                                     // every wave is done with the last stage
+  if (tm_valid > 0) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int m = wm * WM + tm * 16 + (lane & 15);
+      float sc = 1.0f;
+      if (MODE == kDown) {
+        const int prow = (m < rows_valid) ? (grouped ? g.sorted_pairs[row0 + m] : row0 + m) : -1;
+        sc = (prow >= 0) ? g.scale[prow] : 0.0f;
+      }
+      if (MODE == kGateUp) {
+        constexpr int kHalfTN = TN / 2;
+#pragma unroll
+        for (int t = 0; t < kHalfTN; ++t) {
+          const int n = wn * (WN / 2) + t * 16 + (lane >> 4) * 4;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = silu_f32(acc[tm][t][i]) * acc[tm][t + kHalfTN][i];
+          *reinterpret_cast<uint2*>(so + m * OUT_LD + n) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      } else {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int n = wn * WN + tn * 16 + (lane >> 4) * 4;
+          const floatx4 a = acc[tm][tn];
+          *reinterpret_cast<uint2*>(so + m * OUT_LD + n) =
+              uint2{pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3])};
+        }
       }
     }
   }
-
-  // Epilogue: lane holds rows 4*(lane/16)+i of column lane%16 of each sub-tile.
+  __syncthreads();
+  constexpr int kThreads = 64 * NW;
+  constexpr int CPR = OUT_COLS / 8;                    // 16-byte chunks per output row
+  const int col0 = (MODE == kGateUp) ? nt * half : nt * BN;
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    if (tm >= tm_valid) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * WM + tm * 16 + (lane >> 4) * 4 + i;
-      if (r >= rows_valid) continue;
-      if (MODE == kGateUp) {
-        constexpr int kHalfTN = TN / 2;
-        uint16_t* out_row = C + (int64_t)(row0 + r) * g.n_out;
-#pragma unroll
-        for (int t = 0; t < kHalfTN; ++t) {
-          const int col = nt * half + wn * (WN / 2) + t * 16 + (lane & 15);
-          if (col < g.n_out) {
-            const float gv = acc[tm][t][i], uv = acc[tm][t + kHalfTN][i];
-            out_row[col] = f32_to_bf16(silu_f32(gv) * uv);
-          }
-        }
-      } else {
-        const int prow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
-        const float sc = g.scale[prow];
-        uint16_t* out_row = C + (int64_t)prow * g.n_out;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int col = nt * BN + wn * WN + tn * 16 + (lane & 15);
-          if (col < g.n_out) out_row[col] = f32_to_bf16(sc * acc[tm][tn][i]);
-        }
-      }
-    }
+  for (int c = threadIdx.x; c < BM * CPR; c += kThreads) {
+    const int r = c / CPR, j = c % CPR;
+    if (r >= rows_valid || col0 + j * 8 >= g.n_out) continue;
+    int64_t orow;
+    if (MODE == kGateUp) orow = row0 + r;
+    else orow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
+    *reinterpret_cast<uint4*>(C + orow * g.n_out + col0 + j * 8) =
+        *reinterpret_cast<const uint4*>(so + r * OUT_LD + j * 8);
   }
 }
 
