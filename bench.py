@@ -94,7 +94,10 @@ def bench_workload(name, steps, warmup, torch, moe):
     ids = torch.empty((cfg.N, cfg.top_k), dtype=torch.int32, device=dev)
     wts = torch.empty((cfg.N, cfg.top_k), dtype=torch.float32, device=dev)
     sscale = torch.empty(cfg.N, dtype=torch.float32, device=dev) if cfg.I_shared else None
-    gr = moe.moe_align(ids.zero_(), cfg.E, bm)
+    route_scratch = torch.empty(max(1, moe.moe_route_scratch_size(p) // 4), dtype=torch.float32, device=dev)
+    align_scratch = torch.empty(max(1, moe.moe_align_scratch_size(cfg.N * cfg.top_k, cfg.E) // 4),
+                                dtype=torch.int32, device=dev)
+    gr = moe.moe_align(ids.zero_(), cfg.E, bm, align_scratch)
     act = torch.empty((gr.max_rows, cfg.I), dtype=t["x"].dtype, device=dev)
     y = torch.empty((cfg.N * cfg.top_k, cfg.H), dtype=t["x"].dtype, device=dev)
     sact = torch.empty((cfg.N, cfg.I_shared), dtype=t["x"].dtype, device=dev) if cfg.I_shared else None
@@ -102,9 +105,10 @@ def bench_workload(name, steps, warmup, torch, moe):
 
     def staged(e):
         e[0].record()
-        moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob, t["shared_gate"], ids, wts, sscale)
+        moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob, t["shared_gate"], ids, wts, sscale,
+                      route_scratch)
         e[1].record()
-        g2 = moe.moe_align(ids, cfg.E, bm)
+        g2 = moe.moe_align(ids, cfg.E, bm, align_scratch)
         e[2].record()
         moe.moe_gate_up(t["x"], t["w_gate_up"], g2, cfg.top_k, act)
         e[3].record()

@@ -81,8 +81,8 @@ typedef struct moe_workspace_layout {
   int64_t block_m;         /* rows per grouped-GEMM tile */
   int64_t max_rows;        /* capacity of sorted_pairs / act rows */
   int64_t max_tiles;       /* capacity of tile_expert / tile_rows */
-  size_t topk_ids, topk_w, shared_scale;
-  size_t counts, offsets, order, sorted_pairs, tile_expert, tile_rows, num_tiles;
+  size_t route_scratch, topk_ids, topk_w, shared_scale;
+  size_t counts, offsets, order, sorted_pairs, tile_expert, tile_rows, num_tiles, align_scratch;
   size_t act, y, shared_act, shared_y;
   size_t total_bytes;
 } moe_workspace_layout;
@@ -109,10 +109,17 @@ int moe_align_capacity(int64_t num_pairs, int64_t num_experts, int64_t block_m,
  *                      probabilities to the lower expert id
  *   topk_w     [N, k]  float32 out: the probabilities of those experts,
  *                      divided by their sum when norm_topk_prob is set
- * Logits are accumulated in float32; softmax runs over all E in float32. */
+ *   scratch            float32 device array of moe_route_scratch_size bytes
+ *                      (partial logits; overwritten, need not be cleared)
+ * Logits are accumulated in float32 (8 fixed slices of H, summed in slice
+ * order, so a token's routing does not depend on the batch); softmax runs
+ * over all E in float32. */
 int moe_route(const moe_problem* p, const void* x, const void* router_w,
               const void* shared_gate, int32_t* topk_ids, float* topk_w,
-              float* shared_scale, void* stream);
+              float* shared_scale, float* scratch, void* stream);
+
+/* Scratch moe_route needs for p (bytes).  Pure host arithmetic. */
+int moe_route_scratch_size(const moe_problem* p, size_t* bytes);
 
 /* Grouping of the N*k pairs by expert (M03 逐步图 steps 1-3: flatten, stable
  * sort by expert id, per-expert counts and segment starts; the padding to
@@ -130,12 +137,20 @@ int moe_route(const moe_problem* p, const void* x, const void* router_w,
  *                            [t*block_m, (t+1)*block_m) of sorted_pairs)
  *   tile_rows    [max_tiles] int32 out: real (non-sentinel) rows of tile t
  *   num_tiles    [1]         int32 out: number of tiles written
- * Capacities come from moe_align_capacity.  block_m in [1, 1024]. */
+ *   scratch      device array of moe_align_scratch_size bytes (may be NULL
+ *                when that size is 0, i.e. up to 4096 pairs); its contents
+ *                are overwritten, nothing needs to be cleared beforehand
+ * Capacities come from moe_align_capacity.  block_m in [1, 1024].  Ids
+ * outside [0, E) are dropped (not counted, not placed). */
 int moe_align(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k,
               int64_t num_experts, int64_t block_m, int32_t* counts,
               int32_t* offsets, int32_t* order, int32_t* sorted_pairs,
               int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles,
-              void* stream);
+              int32_t* scratch, void* stream);
+
+/* Scratch moe_align needs for num_pairs pairs over num_experts experts.
+ * Pure host arithmetic. */
+int moe_align_scratch_size(int64_t num_pairs, int64_t num_experts, size_t* bytes);
 
 /* Grouped gate/up product with the SwiGLU epilogue (M03 题面速览 expert
  * formula; L1 细节 weight shapes): for every tile row r holding pair p,
@@ -144,7 +159,8 @@ int moe_align(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k,
  *   w_gate_up [E, 2I, H] dtype;  act [max_rows, I] dtype out (sentinel rows
  *   are left unwritten).  Grouping arrays as produced by moe_align with the
  *   same block_m; max_tiles bounds the launch, *num_tiles is read on the
- *   device. */
+ *   device.  block_m: bf16 takes 16, 32, 64, 128 or 320; fp32 any in
+ *   [1, 1024]. */
 int moe_gate_up(const moe_problem* p, const void* x, const void* w_gate_up,
                 const int32_t* sorted_pairs, const int32_t* tile_expert,
                 const int32_t* tile_rows, const int32_t* num_tiles,

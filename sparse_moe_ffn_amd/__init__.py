@@ -5,5 +5,7 @@ The computation lives in hand-written HIP kernels in ``libmoe_mi355x.so``
 it.  Build the library with ``python -m sparse_moe_ffn_amd.build``.
 """
 from .binding import (MoEError, MoEProblem, Grouping, load_library, problem, problem_from,  # noqa: F401
-                      moe_workspace_size, moe_get_workspace_layout, moe_align_capacity, moe_route,
+                      moe_workspace_size, moe_get_workspace_layout, moe_align_capacity, moe_align_scratch_size,
+                      moe_route_scratch_size,
+                      moe_route,
                       moe_align, moe_gate_up, moe_down, moe_shared_expert, moe_combine, moe_forward)

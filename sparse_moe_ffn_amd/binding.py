@@ -40,8 +40,10 @@ class MoEProblem(ctypes.Structure):
 
 class MoEWorkspaceLayout(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int64), ("max_rows", ctypes.c_int64), ("max_tiles", ctypes.c_int64)] + [
-        (n, ctypes.c_size_t) for n in ("topk_ids", "topk_w", "shared_scale", "counts", "offsets", "order",
-                                       "sorted_pairs", "tile_expert", "tile_rows", "num_tiles", "act", "y",
+        (n, ctypes.c_size_t) for n in ("route_scratch", "topk_ids", "topk_w", "shared_scale", "counts", "offsets",
+                                       "order",
+                                       "sorted_pairs", "tile_expert", "tile_rows", "num_tiles", "align_scratch",
+                                       "act", "y",
                                        "shared_act", "shared_y", "total_bytes")]
 
 
@@ -62,8 +64,10 @@ def load_library() -> ctypes.CDLL:
             "moe_workspace_size": [PP, ctypes.POINTER(ctypes.c_size_t)],
             "moe_get_workspace_layout": [PP, ctypes.POINTER(MoEWorkspaceLayout)],
             "moe_align_capacity": [_I64, _I64, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)],
-            "moe_route": [PP, _P, _P, _P, _P, _P, _P, _P],
-            "moe_align": [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P],
+            "moe_route": [PP, _P, _P, _P, _P, _P, _P, _P, _P],
+            "moe_route_scratch_size": [PP, ctypes.POINTER(ctypes.c_size_t)],
+            "moe_align": [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+            "moe_align_scratch_size": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
             "moe_gate_up": [PP, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P],
             "moe_down": [PP, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P],
             "moe_shared_expert": [PP, _P, _P, _P, _P, _P, _P, _P],
@@ -142,8 +146,14 @@ def moe_align_capacity(num_pairs: int, num_experts: int, block_m: int):
     return r.value, t.value
 
 
+def moe_route_scratch_size(p: MoEProblem) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().moe_route_scratch_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
 def moe_route(x, router_w, top_k, norm_topk_prob, shared_gate=None, topk_ids=None, topk_w=None,
-              shared_scale=None):
+              shared_scale=None, scratch=None):
     """(topk_ids int32 [N,k], topk_w float32 [N,k], shared_scale float32 [N] or None)."""
     x = _gpu(x, "x")
     dev = x.device
@@ -161,9 +171,12 @@ def moe_route(x, router_w, top_k, norm_topk_prob, shared_gate=None, topk_ids=Non
         topk_ids = torch.empty((N, top_k), dtype=torch.int32, device=dev)
     if topk_w is None:
         topk_w = torch.empty((N, top_k), dtype=torch.float32, device=dev)
+    if scratch is None:
+        scratch = torch.empty(max(1, moe_route_scratch_size(p) // 4), dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_route(ctypes.byref(p), _ptr(x), _ptr(router_w), _ptr(shared_gate),
-                                        _ptr(topk_ids), _ptr(topk_w), _ptr(shared_scale), _stream(dev)))
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(shared_scale), _ptr(scratch),
+                                        _stream(dev)))
     return topk_ids, topk_w, shared_scale
 
 
@@ -181,7 +194,13 @@ class Grouping:
     max_tiles: int
 
 
-def moe_align(topk_ids, num_experts: int, block_m: int) -> Grouping:
+def moe_align_scratch_size(num_pairs: int, num_experts: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().moe_align_scratch_size(num_pairs, num_experts, ctypes.byref(n)))
+    return n.value
+
+
+def moe_align(topk_ids, num_experts: int, block_m: int, scratch=None) -> Grouping:
     topk_ids = _gpu(topk_ids, "topk_ids", torch.int32)
     dev = topk_ids.device
     N, k = topk_ids.shape
@@ -191,11 +210,14 @@ def moe_align(topk_ids, num_experts: int, block_m: int) -> Grouping:
     g = Grouping(torch.empty(num_experts, **i32), torch.empty(num_experts + 1, **i32), torch.empty(P, **i32),
                  torch.empty(max_rows, **i32), torch.empty(max_tiles, **i32), torch.empty(max_tiles, **i32),
                  torch.empty(1, **i32), block_m, max_rows, max_tiles)
+    need = moe_align_scratch_size(P, num_experts)
+    if scratch is None and need:
+        scratch = torch.empty(need // 4, **i32)
     with torch.cuda.device(dev):
         _check(load_library().moe_align(_ptr(topk_ids), N, k, num_experts, block_m, _ptr(g.counts),
                                         _ptr(g.offsets), _ptr(g.order), _ptr(g.sorted_pairs),
                                         _ptr(g.tile_expert), _ptr(g.tile_rows), _ptr(g.num_tiles),
-                                        _stream(dev)))
+                                        _ptr(scratch) if need else None, _stream(dev)))
     return g
 
 

@@ -1,4 +1,4 @@
-// Align kernel: stable grouping of the N*k (token, slot) pairs by expert id,
+// Align kernels: stable grouping of the N*k (token, slot) pairs by expert id,
 // each expert's segment padded to the GEMM tile height.
 //
 // Follows "M03 · Sparse MoE：路由、按 expert 分组计算、shared expert",
@@ -7,21 +7,25 @@
 // the remark there that this bookkeeping is what aligning tokens to a block
 // does in a fused MoE.
 //
-// One workgroup of 16 waves.  The pair list is cut into 16 contiguous
-// chunks, one per wave.
-//   pass 1: per-wave histograms with LDS atomics (counts only);
-//   scan:   per-expert exclusive prefix over the waves (each wave's base
-//           inside an expert), then over experts for the unpadded segment
-//           starts, the tile starts and the padded row starts;
-//   pass 2: each wave walks its chunk 64 pairs at a time; lanes holding the
-//           same expert find each other with one ballot per id bit, a lane's
-//           rank is the number of matching lanes below it, and the highest
-//           matching lane advances the wave's running position for that
-//           expert.  Chunks are in pair order and lanes are in pair order, so
-//           positions are ascending in the pair index: the sort is stable
-//           without comparing anything.
+// The pair list is cut into chunks of kChunk pairs and each chunk into 16
+// contiguous wave ranges.  Positions are built from counts only:
+//   histogram: per-range counts with LDS atomics;
+//   scan:      per-expert exclusive prefixes over the ranges (each range's
+//              base inside its expert), then over the experts for the
+//              unpadded segment starts, the tile starts and the padded rows;
+//   scatter:   each wave walks its range 64 pairs at a time; lanes holding
+//              the same expert find each other with one ballot per id bit, a
+//              lane's rank is the number of matching lanes below it, and the
+//              highest matching lane advances the running position.  Ranges
+//              are in pair order and lanes are in pair order, so positions are
+//              ascending in the pair index: the sort is stable without
+//              comparing anything.
 // Atomics only count; every position comes from prefix sums, so the result
 // is the same on every run.
+//
+// One chunk (<= 4096 pairs): a single workgroup does everything.  More: three
+// launches (count per chunk, scan in one workgroup, scatter per chunk) with
+// the per-chunk counts in a caller-provided scratch array.
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -29,45 +33,152 @@ namespace moe {
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
-constexpr int kAlignUnroll = 8;
+constexpr int kAlignUnroll = 4;
+constexpr int kChunk = kAlignWaves * kWave * kAlignUnroll;     // pairs per chunk (4096)
 
-__global__ __launch_bounds__(kAlignThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int BM, int nbits, int32_t* __restrict__ counts,
+// Expert id of pair p, or -1 past the end / outside [0, E) (dropped).
+__device__ __forceinline__ int pair_expert(const int32_t* ids, int p, int end, int E) {
+  const int v = (p < end) ? ids[p] : -1;
+  return (v < E) ? v : -1;
+}
+
+// Lanes of this wave holding the same valid expert id as this lane.
+__device__ __forceinline__ unsigned long long match_lanes(int e, int nbits) {
+  const bool valid = e >= 0;
+  unsigned long long match = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const unsigned long long m = __ballot(bit);
+    match &= bit ? m : ~m;
+  }
+  return match;
+}
+
+// Histogram of pairs [beg, end) into h[e] (LDS atomics, counts only).
+__device__ __forceinline__ void count_range(const int32_t* ids, int beg, int end, int E, int* h) {
+  const int lane = lane_id();
+  for (int p0 = beg; p0 < end; p0 += kWave * kAlignUnroll) {
+    int e[kAlignUnroll];
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) e[u] = pair_expert(ids, p0 + u * kWave + lane, end, E);
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u)
+      if (e[u] >= 0) atomicAdd(&h[e[u]], 1);
+  }
+}
+
+// Stable scatter of pairs [beg, end): pos[e] holds the running position of
+// expert e inside its segment for this range (advanced in place).
+__device__ __forceinline__ void scatter_range(const int32_t* ids, int beg, int end, int E, int BM, int nbits,
+                                              int* pos, const int* seg_start, const int* tile_start,
+                                              int32_t* order, int32_t* sorted_pairs) {
+  const int lane = lane_id();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int p0 = beg; p0 < end; p0 += kWave * kAlignUnroll) {
+    int ev[kAlignUnroll];
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) ev[u] = pair_expert(ids, p0 + u * kWave + lane, end, E);
+#pragma unroll
+    for (int u = 0; u < kAlignUnroll; ++u) {
+      const int p = p0 + u * kWave + lane;
+      const int e = ev[u];
+      const unsigned long long match = match_lanes(e, nbits);
+      if (e >= 0) {
+        const int rank = __popcll(match & below);
+        const int at = pos[e] + rank;
+        order[seg_start[e] + at] = p;
+        sorted_pairs[tile_start[e] * BM + at] = p;
+        if ((match >> lane) == 1ull) pos[e] = at + 1;          // highest matching lane
+      }
+    }
+  }
+}
+
+// Wave 0: exclusive scans of cnt[] (rows) and of its tile counts over the
+// experts; writes seg_start, tile_start, offsets and num_tiles.
+__device__ __forceinline__ void scan_experts(const int* cnt, int E, int BM, int* seg_start, int* tile_start,
+                                             int32_t* offsets, int32_t* num_tiles) {
+  const int lane = lane_id();
+  int carry_rows = 0, carry_tiles = 0;
+  for (int e0 = 0; e0 < E; e0 += kWave) {
+    const int e = e0 + lane;
+    const int c = (e < E) ? cnt[e] : 0;
+    const int nt = (c + BM - 1) / BM;
+    int ic = c, it = nt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int uc = __shfl_up(ic, o, kWave);
+      const int ut = __shfl_up(it, o, kWave);
+      if (lane >= o) { ic += uc; it += ut; }
+    }
+    if (e < E) {
+      seg_start[e] = carry_rows + ic - c;
+      tile_start[e] = carry_tiles + it - nt;
+      offsets[e] = carry_rows + ic - c;
+    }
+    carry_rows += __shfl(ic, kWave - 1, kWave);
+    carry_tiles += __shfl(it, kWave - 1, kWave);
+  }
+  if (lane == 0) {
+    offsets[E] = carry_rows;
+    num_tiles[0] = carry_tiles;
+  }
+}
+
+// Tile table and sentinel padding, by the whole workgroup.
+__device__ __forceinline__ void fill_tiles(const int* cnt, const int* tile_start, int E, int BM, int P,
+                                           int total_tiles, int32_t* sorted_pairs, int32_t* tile_expert,
+                                           int32_t* tile_rows) {
+  for (int t = threadIdx.x; t < total_tiles; t += blockDim.x) {
+    int lo = 0, hi = E - 1;                  // last expert whose tile range starts at or before t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    int e = lo;
+    while (e > 0 && cnt[e] == 0) --e;        // empty experts own no tiles
+    tile_expert[t] = e;
+    tile_rows[t] = min(BM, cnt[e] - (t - tile_start[e]) * BM);
+  }
+  // Sentinel padding: a group of threads per expert, each taking every
+  // tpe-th padding row of it.
+  const int tpe = max(1, (int)blockDim.x / E);
+  const int groups = blockDim.x / tpe;
+  for (int e = threadIdx.x / tpe; e < E; e += groups) {
+    const int c = cnt[e];
+    const int padded = ((c + BM - 1) / BM) * BM;
+    int32_t* seg = sorted_pairs + (int64_t)tile_start[e] * BM;
+    for (int r = c + (int)(threadIdx.x % tpe); r < padded; r += tpe) seg[r] = P;
+  }
+}
+
+__device__ __forceinline__ int nbits_of(int E) {
+  int n = 0;
+  while ((1 << n) < E) ++n;
+  return n;
+}
+
+// ------------------------------------------------------------ one workgroup
+
+__global__ __launch_bounds__(kAlignThreads) void align_single_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int BM, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ order, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_rows, int32_t* __restrict__ num_tiles) {
   __shared__ int hist[kAlignWaves][kMaxExperts];   // per-wave counts, then per-wave bases
   __shared__ int cnt[kMaxExperts];
   __shared__ int seg_start[kMaxExperts];
   __shared__ int tile_start[kMaxExperts];
-
   const int tid = threadIdx.x;
-  const int lane = lane_id();
   const int wave = tid / kWave;
+  const int nbits = nbits_of(E);
 
   for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
   __syncthreads();
-
-  // Chunk of this wave: a multiple of 64 pairs.
-  const int chunk = ((P + kAlignWaves * kWave - 1) / (kAlignWaves * kWave)) * kWave;
-  const int beg = min(P, wave * chunk);
-  const int end = min(P, beg + chunk);
-
-  // pass 1: histogram (loads issued in batches so they overlap)
-  for (int p0 = beg; p0 < end; p0 += kWave * kAlignUnroll) {
-    int e[kAlignUnroll];
-#pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u) {
-      const int p = p0 + u * kWave + lane;
-      const int v = (p < end) ? ids[p] : -1;
-      e[u] = (v < E) ? v : -1;                          // ids outside [0, E) are dropped
-    }
-#pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u)
-      if (e[u] >= 0) atomicAdd(&hist[wave][e[u]], 1);
-  }
+  const int range = ((P + kAlignWaves * kWave - 1) / (kAlignWaves * kWave)) * kWave;
+  const int beg = min(P, wave * range);
+  const int end = min(P, beg + range);
+  count_range(ids, beg, end, E, hist[wave]);
   __syncthreads();
-
-  // per-expert: exclusive base of every wave inside the expert, and the total
   for (int e = tid; e < E; e += kAlignThreads) {
     int run = 0;
     for (int w = 0; w < kAlignWaves; ++w) {
@@ -76,93 +187,126 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       run += c;
     }
     cnt[e] = run;
+    counts[e] = run;
   }
   __syncthreads();
+  if (wave == 0) scan_experts(cnt, E, BM, seg_start, tile_start, offsets, num_tiles);
+  __syncthreads();
+  scatter_range(ids, beg, end, E, BM, nbits, hist[wave], seg_start, tile_start, order, sorted_pairs);
+  const int total = tile_start[E - 1] + (cnt[E - 1] + BM - 1) / BM;
+  fill_tiles(cnt, tile_start, E, BM, P, total, sorted_pairs, tile_expert, tile_rows);
+}
 
-  // exclusive scans over experts (wave 0, 64 experts per step)
-  if (wave == 0) {
-    int carry_rows = 0, carry_tiles = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const int e = e0 + lane;
-      const int c = (e < E) ? cnt[e] : 0;
-      const int nt = (c + BM - 1) / BM;
-      int ic = c, it = nt;
+// ------------------------------------------------------------ many chunks
+
+// Per-chunk expert histogram -> chunk_counts[chunk][E].
+__global__ __launch_bounds__(kAlignThreads) void align_count_kernel(const int32_t* __restrict__ ids, int P,
+                                                                     int E, int32_t* __restrict__ chunk_counts) {
+  __shared__ int h[kMaxExperts];
+  for (int i = threadIdx.x; i < E; i += kAlignThreads) h[i] = 0;
+  __syncthreads();
+  const int c0 = blockIdx.x * kChunk;
+  const int wave = threadIdx.x / kWave;
+  const int range = kChunk / kAlignWaves;
+  const int beg = min(P, c0 + wave * range);
+  const int end = min(P, beg + range);
+  count_range(ids, beg, end, E, h);
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += kAlignThreads) chunk_counts[(int64_t)blockIdx.x * E + i] = h[i];
+}
+
+// chunk_counts -> per-chunk bases (in place), counts, offsets, tile starts
+// (scratch_tile_start[E]), tile table, padding, num_tiles.
+__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
+    int P, int E, int BM, int nchunks, int32_t* __restrict__ chunk_counts, int32_t* __restrict__ tile_start_out,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_rows, int32_t* __restrict__ num_tiles) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int seg_start[kMaxExperts];
+  __shared__ int tile_start[kMaxExperts];
+  __shared__ int total_tiles;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int run = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {          // 8 independent loads in flight
+      int v[8];
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int uc = __shfl_up(ic, o, kWave);
-        const int ut = __shfl_up(it, o, kWave);
-        if (lane >= o) { ic += uc; it += ut; }
+      for (int u = 0; u < 8; ++u) v[u] = (c0 + u < nchunks) ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < nchunks) chunk_counts[(int64_t)(c0 + u) * E + e] = run;
+        run += v[u];
       }
-      if (e < E) {
-        seg_start[e] = carry_rows + ic - c;
-        tile_start[e] = carry_tiles + it - nt;
-      }
-      carry_rows += __shfl(ic, kWave - 1, kWave);
-      carry_tiles += __shfl(it, kWave - 1, kWave);
     }
-    if (lane == 0) {
-      offsets[E] = carry_rows;
-      num_tiles[0] = carry_tiles;
+    cnt[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  if (tid < kWave) scan_experts(cnt, E, BM, seg_start, tile_start, offsets, num_tiles);
+  __syncthreads();
+  for (int e = tid; e < E; e += kAlignThreads) tile_start_out[e] = tile_start[e];
+  if (tid == 0) total_tiles = tile_start[E - 1] + (cnt[E - 1] + BM - 1) / BM;
+  __syncthreads();
+  fill_tiles(cnt, tile_start, E, BM, P, total_tiles, sorted_pairs, tile_expert, tile_rows);
+}
+
+// Stable scatter of one chunk, starting from the chunk's bases.
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int BM, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ tile_start_in, const int32_t* __restrict__ offsets, int32_t* __restrict__ order,
+    int32_t* __restrict__ sorted_pairs) {
+  __shared__ int hist[kAlignWaves][kMaxExperts];
+  __shared__ int seg_start[kMaxExperts];
+  __shared__ int tile_start[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
+  for (int e = tid; e < E; e += kAlignThreads) {
+    seg_start[e] = offsets[e];
+    tile_start[e] = tile_start_in[e];
+  }
+  __syncthreads();
+  const int c0 = blockIdx.x * kChunk;
+  const int range = kChunk / kAlignWaves;
+  const int beg = min(P, c0 + wave * range);
+  const int end = min(P, beg + range);
+  count_range(ids, beg, end, E, hist[wave]);
+  __syncthreads();
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int run = chunk_base[(int64_t)blockIdx.x * E + e];
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int c = hist[w][e];
+      hist[w][e] = run;
+      run += c;
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kAlignThreads) {
-    counts[e] = cnt[e];
-    offsets[e] = seg_start[e];
-  }
+  scatter_range(ids, beg, end, E, BM, nbits_of(E), hist[wave], seg_start, tile_start, order, sorted_pairs);
+}
 
-  // pass 2: stable scatter
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int p0 = beg; p0 < end; p0 += kWave * kAlignUnroll) {
-    int ev[kAlignUnroll];
-#pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u) {
-      const int p = p0 + u * kWave + lane;
-      const int v = (p < end) ? ids[p] : -1;
-      ev[u] = (v < E) ? v : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u) {
-      const int p = p0 + u * kWave + lane;
-      const int e = ev[u];
-      const bool valid = e >= 0;
-      unsigned long long match = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = valid && ((e >> b) & 1);
-        const unsigned long long m = __ballot(bit);
-        match &= bit ? m : ~m;
-      }
-      if (valid) {
-        const int rank = __popcll(match & below);
-        const int pos = hist[wave][e] + rank;
-        order[seg_start[e] + pos] = p;
-        sorted_pairs[tile_start[e] * BM + pos] = p;
-        if ((match >> lane) == 1ull) hist[wave][e] = pos + 1;   // highest matching lane
-      }
-    }
-  }
-
-  // padding rows and tile table, one expert per thread
-  for (int e = tid; e < E; e += kAlignThreads) {
-    const int c = cnt[e];
-    const int t0 = tile_start[e];
-    const int nt = (c + BM - 1) / BM;
-    for (int t = 0; t < nt; ++t) {
-      tile_expert[t0 + t] = e;
-      tile_rows[t0 + t] = min(BM, c - t * BM);
-    }
-    for (int r = c; r < nt * BM; ++r) sorted_pairs[t0 * BM + r] = P;
-  }
+int64_t align_scratch_ints(int64_t num_pairs, int64_t num_experts) {
+  const int64_t nchunks = (num_pairs + kChunk - 1) / kChunk;
+  return nchunks <= 1 ? 0 : nchunks * num_experts + num_experts;
 }
 
 hipError_t launch_align(const int32_t* ids, int64_t num_pairs, int64_t num_experts, int64_t block_m,
                         int32_t* counts, int32_t* offsets, int32_t* order, int32_t* sorted_pairs,
-                        int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles, hipStream_t s) {
-  int nbits = 0;
-  while ((1ll << nbits) < num_experts) ++nbits;
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, (int)num_pairs,
-                     (int)num_experts, (int)block_m, nbits, counts, offsets, order, sorted_pairs,
-                     tile_expert, tile_rows, num_tiles);
+                        int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles, int32_t* scratch,
+                        hipStream_t s) {
+  const int P = (int)num_pairs, E = (int)num_experts, BM = (int)block_m;
+  const int nchunks = (P + kChunk - 1) / kChunk;
+  if (nchunks <= 1) {
+    hipLaunchKernelGGL(align_single_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, P, E, BM, counts, offsets,
+                       order, sorted_pairs, tile_expert, tile_rows, num_tiles);
+    return hipGetLastError();
+  }
+  int32_t* chunk_counts = scratch;
+  int32_t* tile_start = scratch + (int64_t)nchunks * E;
+  hipLaunchKernelGGL(align_count_kernel, dim3(nchunks), dim3(kAlignThreads), 0, s, ids, P, E, chunk_counts);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kAlignThreads), 0, s, P, E, BM, nchunks, chunk_counts,
+                     tile_start, counts, offsets, sorted_pairs, tile_expert, tile_rows, num_tiles);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kAlignThreads), 0, s, ids, P, E, BM, chunk_counts,
+                     tile_start, offsets, order, sorted_pairs);
   return hipGetLastError();
 }
 

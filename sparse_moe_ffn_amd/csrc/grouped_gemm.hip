@@ -36,8 +36,7 @@
 
 namespace moe {
 
-constexpr int kBK = 64;                 // K elements per stage: 128-byte bf16 rows
-constexpr int kRowsPerDma = 8;          // one wave-wide 16-byte-per-lane DMA fills 8 rows
+constexpr int kDmaBytes = 64 * 16;      // one wave-wide DMA: 16 bytes per lane
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -68,15 +67,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Element offset of 16-byte chunk `chunk` of row `row` in a staged tile: the
-// chunk index is XOR-ed with the row's low bits so that 16 lanes reading one
-// chunk column of 16 consecutive rows spread over the banks.
+// Element offset of 16-byte chunk `chunk` of row `row` in a staged tile of
+// BK-element rows.  The chunk index is XOR-ed with bits of the row so that
+// the 8 lanes of one LDS read phase (8 consecutive rows, one chunk column)
+// land in 8 different 16-byte bank groups of a 128-byte bank window:
+// 128-byte rows (BK = 64) use the row's low 3 bits; 64-byte rows (BK = 32)
+// pair rows (two rows fill a window) and use bits 1-2.
+template <int BK>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
+  if constexpr (BK == 64) return row * BK + ((chunk ^ (row & 7)) << 3);
+  else return row * BK + ((chunk ^ ((row >> 1) & 3)) << 3);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int PFD, int MODE>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  constexpr int kCpr = BK / 8;                      // 16-byte chunks per staged row
+  constexpr int kRowsPerDma = kDmaBytes / (BK * 2); // rows one wave-wide DMA fills
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M;
   constexpr int WN = BN / WAVES_N;
@@ -90,7 +97,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   static_assert(NDMA % NW == 0, "stage rows must split evenly over the waves");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES][ROWS * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES][ROWS * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t pf_sink[kDmaBytes / 2];
 
   const bool grouped = g.sorted_pairs != nullptr;
   const int half = BN / 2;
@@ -132,8 +140,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
 #pragma unroll
   for (int q = 0; q < PER_WAVE; ++q) {
     const int gi = wave + NW * q;
-    const int r = gi * kRowsPerDma + (lane >> 3);
-    const int chunk = (lane & 7) ^ (r & 7);
+    const int r = gi * kRowsPerDma + lane / kCpr;
+    const int slot = lane % kCpr;
+    const int chunk = (swz<BK>(r, slot) - r * BK) >> 3;   // the swizzle is its own inverse
     const uint16_t* row_ptr;
     if (r < BM) {
       int64_t src_row;
@@ -166,14 +175,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
     src[q] = row_ptr + chunk * 8;
   }
 
+  // L2 warm-up (PFD > 0): with each stage's DMAs a wave also touches the
+  // cache lines of its share of the weight rows PFD stages further on, with
+  // one DMA into a scratch LDS line.  By the time that stage's real DMA runs,
+  // its weight lines are in L2, so the short LDS pipeline only has to cover
+  // L2 latency.  Every stage's DMAs are preceded by exactly one such touch,
+  // so the vmcnt arithmetic stays static.
+  constexpr int kPfRows = BN / NW;                   // weight rows per wave
+  constexpr int kPfLanesPerRow = 64 / kPfRows;       // lanes spread over each row's line
+  static_assert(PFD == 0 || (kPfRows >= 1 && kPfRows <= 64 && 64 % kPfRows == 0), "prefetch split");
+  const uint16_t* pf_src = nullptr;
+  if constexpr (PFD > 0) {
+    const int j = wave * kPfRows + (lane / kPfLanesPerRow);
+    int64_t wrow;
+    if (MODE == kGateUp)
+      wrow = (j < half) ? min((int64_t)nt * half + j, (int64_t)g.n_out - 1)
+                        : min((int64_t)g.n_out + nt * half + (j - half), b_rows - 1);
+    else
+      wrow = min((int64_t)nt * BN + j, b_rows - 1);
+    pf_src = B + wrow * K + (lane % kPfLanesPerRow) * (BK / kPfLanesPerRow);
+  }
+  const int nk = K / BK;
   auto issue = [&](int kt, int st) {
+    if constexpr (PFD > 0) dma16(pf_src + min(kt + PFD, nk - 1) * BK, lds_addr(pf_sink));
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q)
-      dma16(src[q] + kt * kBK, lds_addr(&smem[st][(wave + NW * q) * kRowsPerDma * kBK]));
+      dma16(src[q] + kt * BK, lds_addr(&smem[st][(wave + NW * q) * kRowsPerDma * BK]));
   };
+  constexpr int kPerStage = PER_WAVE + (PFD > 0 ? 1 : 0);
   auto wait_stage = [&](int ahead) {                 // ahead: stages issued past the current one
-    if (STAGES >= 4 && ahead >= 2) wait_vmcnt<((STAGES >= 4) ? 2 : 0) * PER_WAVE>();
-    else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<((STAGES >= 3) ? 1 : 0) * PER_WAVE>();
+    if (STAGES >= 4 && ahead >= 2) wait_vmcnt<((STAGES >= 4) ? 2 : 0) * kPerStage>();
+    else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<((STAGES >= 3) ? 1 : 0) * kPerStage>();
     else wait_vmcnt<0>();
   };
 
@@ -199,7 +231,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // of the DMAs and take part in every barrier, but run a copy of the loop
   // without matrix work (choosing the copy outside the loop keeps both
   // bodies branch-free, so the accumulators stay in AGPRs).
-  const int nk = K / kBK;
   auto main_loop = [&](auto compute) {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
@@ -210,17 +241,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
       if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
       if constexpr (decltype(compute)::value) {
         const uint16_t* As = smem[kt % STAGES];
-        const uint16_t* Bs = As + BM * kBK;
+        const uint16_t* Bs = As + BM * BK;
 #pragma unroll
-        for (int kk = 0; kk < kBK / 32; ++kk) {
+        for (int kk = 0; kk < BK / 32; ++kk) {
           const int ch = kk * 4 + (lane >> 4);
           uint4 af[TM], bfr[TN];
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn)
-            bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz(b_tile_row(tn), ch));
+            bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz<BK>(b_tile_row(tn), ch));
 #pragma unroll
           for (int tm = 0; tm < TM; ++tm)
-            af[tm] = *reinterpret_cast<const uint4*>(As + swz(wm * WM + tm * 16 + (lane & 15), ch));
+            af[tm] = *reinterpret_cast<const uint4*>(As + swz<BK>(wm * WM + tm * 16 + (lane & 15), ch));
 #pragma unroll
           for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -242,52 +273,62 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // 16-byte stores.
   constexpr int OUT_COLS = (MODE == kGateUp) ? BN / 2 : BN;
   constexpr int OUT_LD = OUT_COLS + 8;                 // staged row pitch (+16 B against bank conflicts)
-  static_assert(BM * OUT_LD * 2 <= (int)sizeof(smem), "output tile must fit the LDS");
+  // Rows staged per pass: whole wave rows, as many as fit in the LDS.
+  constexpr int kFitRows = (int)sizeof(smem) / (OUT_LD * 2);
+  constexpr int EPI_ROWS = (kFitRows >= BM) ? BM : (kFitRows / WM) * WM;
+  static_assert(EPI_ROWS >= WM, "one wave row of the output tile must fit the LDS");
+  constexpr int kThreads = 64 * NW;
+  constexpr int CPR = OUT_COLS / 8;                    // 16-byte chunks per output row
   uint16_t* so = &smem[0][0];
-  __syncthreads();                                     // every wave is done with the last stage
-  if (tm_valid > 0) {
+  const int col0 = (MODE == kGateUp) ? nt * half : nt * BN;
+  uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
+  for (int e0 = 0; e0 < BM; e0 += EPI_ROWS) {
+    __syncthreads();                                   // LDS free: last stage or last pass consumed
+    const bool mine = tm_valid > 0 && wm * WM >= e0 && wm * WM < e0 + EPI_ROWS;
+    if (mine) {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int m = wm * WM + tm * 16 + (lane & 15);
-      float sc = 1.0f;
-      if (MODE == kDown) {
-        const int prow = (m < rows_valid) ? (grouped ? g.sorted_pairs[row0 + m] : row0 + m) : -1;
-        sc = (prow >= 0) ? g.scale[prow] : 0.0f;
-      }
-      if (MODE == kGateUp) {
-        constexpr int kHalfTN = TN / 2;
-#pragma unroll
-        for (int t = 0; t < kHalfTN; ++t) {
-          const int n = wn * (WN / 2) + t * 16 + (lane >> 4) * 4;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = silu_f32(acc[tm][t][i]) * acc[tm][t + kHalfTN][i];
-          *reinterpret_cast<uint2*>(so + m * OUT_LD + n) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int tm = 0; tm < TM; ++tm) {
+        const int m = wm * WM + tm * 16 + (lane & 15);
+        const int ml = m - e0;
+        float sc = 1.0f;
+        if (MODE == kDown) {
+          const int prow = (m < rows_valid) ? (grouped ? g.sorted_pairs[row0 + m] : row0 + m) : -1;
+          sc = (prow >= 0) ? g.scale[prow] : 0.0f;
         }
-      } else {
+        if (MODE == kGateUp) {
+          constexpr int kHalfTN = TN / 2;
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int n = wn * WN + tn * 16 + (lane >> 4) * 4;
-          const floatx4 a = acc[tm][tn];
-          *reinterpret_cast<uint2*>(so + m * OUT_LD + n) =
-              uint2{pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3])};
+          for (int t = 0; t < kHalfTN; ++t) {
+            const int n = wn * (WN / 2) + t * 16 + (lane >> 4) * 4;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = silu_f32(acc[tm][t][i]) * acc[tm][t + kHalfTN][i];
+            *reinterpret_cast<uint2*>(so + ml * OUT_LD + n) =
+                uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+        } else {
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const int n = wn * WN + tn * 16 + (lane >> 4) * 4;
+            const floatx4 a = acc[tm][tn];
+            *reinterpret_cast<uint2*>(so + ml * OUT_LD + n) =
+                uint2{pack_bf16x2(sc * a[0], sc * a[1]), pack_bf16x2(sc * a[2], sc * a[3])};
+          }
         }
       }
     }
-  }
-  __syncthreads();
-  constexpr int kThreads = 64 * NW;
-  constexpr int CPR = OUT_COLS / 8;                    // 16-byte chunks per output row
-  const int col0 = (MODE == kGateUp) ? nt * half : nt * BN;
-  uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
-  for (int c = threadIdx.x; c < BM * CPR; c += kThreads) {
-    const int r = c / CPR, j = c % CPR;
-    if (r >= rows_valid || col0 + j * 8 >= g.n_out) continue;
-    int64_t orow;
-    if (MODE == kGateUp) orow = row0 + r;
-    else orow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
-    *reinterpret_cast<uint4*>(C + orow * g.n_out + col0 + j * 8) =
-        *reinterpret_cast<const uint4*>(so + r * OUT_LD + j * 8);
+    __syncthreads();
+    const int rows_here = min(EPI_ROWS, rows_valid - e0);
+    for (int c = threadIdx.x; c < rows_here * CPR; c += kThreads) {
+      const int rl = c / CPR, j = c % CPR;
+      if (col0 + j * 8 >= g.n_out) continue;
+      const int r = e0 + rl;
+      int64_t orow;
+      if (MODE == kGateUp) orow = row0 + r;
+      else orow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
+      *reinterpret_cast<uint4*>(C + orow * g.n_out + col0 + j * 8) =
+          *reinterpret_cast<const uint4*>(so + rl * OUT_LD + j * 8);
+    }
   }
 }
 
@@ -343,12 +384,13 @@ __global__ __launch_bounds__(kF32Threads) void grouped_gemm_f32_kernel(GemmProbl
 
 // ---------------------------------------------------------------- launchers
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int PFD, int MODE>
 static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
+  if (g.block_m != BM) return hipErrorInvalidValue;   // tiles must be laid out for this height
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
   const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, WAVES_M, WAVES_N, STAGES, MODE>),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, PFD, MODE>),
                      dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
   return hipGetLastError();
 }
@@ -362,10 +404,11 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     return hipGetLastError();
   }
   switch (g.block_m) {
-    case 16: return launch_bf16<16, 128, 1, 2, 4, MODE>(g, s);
-    case 32: return launch_bf16<32, 128, 1, 4, 4, MODE>(g, s);
-    case 64: return launch_bf16<64, 256, 1, 4, 3, MODE>(g, s);
-    case 128: return launch_bf16<128, 256, 2, 2, 3, MODE>(g, s);
+    case 16: return launch_bf16<16, 128, 64, 1, 2, 4, 0, MODE>(g, s);
+    case 32: return launch_bf16<32, 128, 64, 1, 4, 4, 0, MODE>(g, s);
+    case 64: return launch_bf16<64, 256, 64, 1, 4, 3, 0, MODE>(g, s);
+    case 128: return launch_bf16<128, 256, 64, 2, 4, 3, 0, MODE>(g, s);
+    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 0, MODE>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

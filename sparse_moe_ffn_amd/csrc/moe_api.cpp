@@ -83,12 +83,13 @@ int64_t choose_block_m(const moe_problem* p) {
   if (avg < 24) return 16;
   if (avg < 48) return 32;
   if (avg < 96) return 64;
-  return 128;
+  if (avg < 192) return 128;
+  return 320;                       // one tile holds a typical prefill expert
 }
 
 bool block_m_supported(int32_t dtype, int64_t bm) {
   if (dtype == MOE_F32) return bm >= 1 && bm <= 1024;
-  return bm == 16 || bm == 32 || bm == 64 || bm == 128;
+  return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 320;
 }
 
 void capacity(int64_t pairs, int64_t experts, int64_t bm, int64_t* rows, int64_t* tiles) {
@@ -110,6 +111,7 @@ void layout_of(const moe_problem* p, moe_workspace_layout* L) {
     off += bytes;
     return r;
   };
+  L->route_scratch = region(moe::route_scratch_floats(N, E, true) * 4);
   L->topk_ids = region(P * 4);
   L->topk_w = region(P * 4);
   L->shared_scale = region(p->shared_inter ? N * 4 : 0);
@@ -120,6 +122,7 @@ void layout_of(const moe_problem* p, moe_workspace_layout* L) {
   L->tile_expert = region(L->max_tiles * 4);
   L->tile_rows = region(L->max_tiles * 4);
   L->num_tiles = region(4);
+  L->align_scratch = region(moe::align_scratch_ints(P, E) * 4);
   L->act = region(L->max_rows * p->inter * es);
   L->y = region(P * p->hidden * es);
   L->shared_act = region(N * p->shared_inter * es);
@@ -174,23 +177,37 @@ int moe_workspace_size(const moe_problem* p, size_t* bytes) {
   return ok();
 }
 
+int moe_route_scratch_size(const moe_problem* p, size_t* bytes) {
+  if (int rc = check_problem(p, kUsesExperts)) return rc;
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  *bytes = (size_t)moe::route_scratch_floats(p->num_tokens, p->num_experts, true) * 4;
+  return ok();
+}
+
 int moe_route(const moe_problem* p, const void* x, const void* router_w, const void* shared_gate,
-              int32_t* topk_ids, float* topk_w, float* shared_scale, void* stream) {
+              int32_t* topk_ids, float* topk_w, float* shared_scale, float* scratch, void* stream) {
   if (int rc = check_problem(p, kUsesExperts)) return rc;
   if (p->num_tokens == 0) return ok();
-  if (!x || !router_w || !topk_ids || !topk_w) return fail(MOE_EINVAL, "NULL tensor");
+  if (!x || !router_w || !topk_ids || !topk_w || !scratch) return fail(MOE_EINVAL, "NULL tensor");
   if (shared_gate && !shared_scale) return fail(MOE_EINVAL, "shared_gate given without shared_scale");
   if (int rc = check_ptrs_bf16(p, {x, router_w, shared_gate})) return rc;
   if (int rc = hip_status(moe::launch_route(*p, x, router_w, shared_gate, topk_ids, topk_w,
-                                            shared_scale, (hipStream_t)stream), "route"))
+                                            shared_scale, scratch, (hipStream_t)stream), "route"))
     return rc;
+  return ok();
+}
+
+int moe_align_scratch_size(int64_t num_pairs, int64_t num_experts, size_t* bytes) {
+  if (!bytes) return fail(MOE_EINVAL, "bytes is NULL");
+  if (num_pairs < 0 || num_experts < 1) return fail(MOE_EINVAL, "need num_pairs >= 0, num_experts >= 1");
+  *bytes = (size_t)moe::align_scratch_ints(num_pairs, num_experts) * 4;
   return ok();
 }
 
 int moe_align(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k, int64_t num_experts,
               int64_t block_m, int32_t* counts, int32_t* offsets, int32_t* order,
               int32_t* sorted_pairs, int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles,
-              void* stream) {
+              int32_t* scratch, void* stream) {
   if (num_tokens < 0 || top_k < 1 || num_experts < 1) return fail(MOE_EINVAL, "bad sizes");
   if (num_experts > moe::kMaxExperts) return fail(MOE_EUNSUPPORTED, "num_experts > %d", moe::kMaxExperts);
   if (block_m < 1 || block_m > 1024) return fail(MOE_EINVAL, "block_m outside [1, 1024]");
@@ -198,9 +215,11 @@ int moe_align(const int32_t* topk_ids, int64_t num_tokens, int64_t top_k, int64_
   if (!counts || !offsets || !num_tiles) return fail(MOE_EINVAL, "NULL output");
   if (num_tokens > 0 && (!topk_ids || !order || !sorted_pairs || !tile_expert || !tile_rows))
     return fail(MOE_EINVAL, "NULL tensor");
+  if (moe::align_scratch_ints(num_tokens * top_k, num_experts) > 0 && !scratch)
+    return fail(MOE_EINVAL, "this many pairs needs the align scratch array");
   if (int rc = hip_status(moe::launch_align(topk_ids, num_tokens * top_k, num_experts, block_m, counts,
                                             offsets, order, sorted_pairs, tile_expert, tile_rows,
-                                            num_tiles, (hipStream_t)stream), "align"))
+                                            num_tiles, scratch, (hipStream_t)stream), "align"))
     return rc;
   return ok();
 }
@@ -322,14 +341,16 @@ int moe_forward(const moe_problem* p, const void* x, const void* router_w, const
   int32_t* ids = (int32_t*)at(L.topk_ids);
   float* w = (float*)at(L.topk_w);
   float* sscale = shared ? (float*)at(L.shared_scale) : nullptr;
-  if (int rc = moe_route(p, x, router_w, shared ? shared_gate : nullptr, ids, w, sscale, stream)) return rc;
+  if (int rc = moe_route(p, x, router_w, shared ? shared_gate : nullptr, ids, w, sscale,
+                         (float*)at(L.route_scratch), stream))
+    return rc;
   int32_t* sorted = (int32_t*)at(L.sorted_pairs);
   int32_t* texp = (int32_t*)at(L.tile_expert);
   int32_t* trows = (int32_t*)at(L.tile_rows);
   int32_t* ntiles = (int32_t*)at(L.num_tiles);
   if (int rc = moe_align(ids, p->num_tokens, p->top_k, p->num_experts, L.block_m, (int32_t*)at(L.counts),
                          (int32_t*)at(L.offsets), (int32_t*)at(L.order), sorted, texp, trows, ntiles,
-                         stream))
+                         (int32_t*)at(L.align_scratch), stream))
     return rc;
   if (int rc = moe_gate_up(p, x, w_gate_up, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
                            at(L.act), stream))

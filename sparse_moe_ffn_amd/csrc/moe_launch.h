@@ -12,15 +12,20 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 32;
 
 // Router: logits, float32 softmax, top-k, optional renormalisation and the
-// optional shared-expert gate.
+// optional shared-expert gate.  `scratch` holds route_scratch_floats(...)
+// floats of partial logits.
+int64_t route_scratch_floats(int64_t N, int64_t E, bool shared);
 hipError_t launch_route(const moe_problem& p, const void* x, const void* router_w,
                         const void* shared_gate, int32_t* ids, float* w, float* shared_scale,
-                        hipStream_t s);
+                        float* scratch, hipStream_t s);
 
-// Stable grouping of the pairs by expert, padded to block_m.
+// Stable grouping of the pairs by expert, padded to block_m.  `scratch`
+// holds align_scratch_ints(...) int32 values (none for one chunk).
+int64_t align_scratch_ints(int64_t num_pairs, int64_t num_experts);
 hipError_t launch_align(const int32_t* ids, int64_t num_pairs, int64_t num_experts, int64_t block_m,
                         int32_t* counts, int32_t* offsets, int32_t* order, int32_t* sorted_pairs,
-                        int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles, hipStream_t s);
+                        int32_t* tile_expert, int32_t* tile_rows, int32_t* num_tiles, int32_t* scratch,
+                        hipStream_t s);
 
 // One grouped (or dense, when sorted_pairs == nullptr) product.
 struct GemmProblem {

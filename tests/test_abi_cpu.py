@@ -44,8 +44,9 @@ def test_problem_validation_codes():
 def test_workspace_layout_is_ordered_and_aligned():
     for args in ((4096, 2048, 128, 8, 768), (64, 2048, 128, 8, 768), (8192, 2048, 128, 8, 768, 2048), (7, 64, 5, 3, 64)):
         L = moe.moe_get_workspace_layout(moe.problem(*args))
-        offs = [L[k] for k in ("topk_ids", "topk_w", "shared_scale", "counts", "offsets", "order", "sorted_pairs",
-                               "tile_expert", "tile_rows", "num_tiles", "act", "y", "shared_act", "shared_y")]
+        offs = [L[k] for k in ("route_scratch", "topk_ids", "topk_w", "shared_scale", "counts", "offsets", "order", "sorted_pairs",
+                               "tile_expert", "tile_rows", "num_tiles", "align_scratch", "act", "y", "shared_act",
+                               "shared_y")]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         assert L["total_bytes"] >= offs[-1] and L["total_bytes"] % 256 == 0
         assert L["max_rows"] == L["max_tiles"] * L["block_m"]
@@ -53,7 +54,7 @@ def test_workspace_layout_is_ordered_and_aligned():
 
 def test_block_m_follows_rows_per_expert():
     bm = lambda N: moe.moe_get_workspace_layout(moe.problem(N, 2048, 128, 8, 768))["block_m"]
-    assert (bm(64), bm(4096), bm(16384)) == (16, 128, 128)
+    assert (bm(64), bm(1024), bm(4096), bm(16384)) == (16, 64, 320, 320)
 
 
 @pytest.mark.parametrize("pairs,E,bm", [(6, 5, 2), (512, 128, 16), (32768, 128, 128), (3, 10, 64), (0, 4, 16)])
@@ -69,6 +70,12 @@ def test_align_capacity_bounds_every_grouping(pairs, E, bm):
     assert tiles >= worst
 
 
+def test_align_scratch_size():
+    assert moe.moe_align_scratch_size(4096, 128) == 0
+    assert moe.moe_align_scratch_size(4097, 128) == (2 * 128 + 128) * 4
+    assert moe.moe_align_scratch_size(131072, 128) == (32 * 128 + 128) * 4
+
+
 def test_forward_rejects_before_any_hip_call():
     lib = moe.load_library()
     p = moe.problem(16, 64, 4, 2, 64)
@@ -82,8 +89,10 @@ def test_forward_rejects_before_any_hip_call():
     rc = lib.moe_forward(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, None, None, None,
                          fake, fake, 1 << 30, None)
     assert rc == B.MOE_EUNSUPPORTED                          # misaligned bf16
-    rc = lib.moe_align(fake, 4, 2, 4, 0, fake, fake, fake, fake, fake, fake, fake, None)
+    rc = lib.moe_align(fake, 4, 2, 4, 0, fake, fake, fake, fake, fake, fake, fake, None, None)
     assert rc == B.MOE_EINVAL
+    rc = lib.moe_align(fake, 5000, 2, 4, 16, fake, fake, fake, fake, fake, fake, fake, None, None)
+    assert rc == B.MOE_EINVAL and b"scratch" in lib.moe_last_error()   # 10000 pairs need scratch
     rc = lib.moe_gate_up(ctypes.byref(p), fake, fake, fake, fake, fake, fake, 48, 4, fake, None)
     assert rc == B.MOE_EUNSUPPORTED                          # bf16 tile height must be 16/32/64/128
     # empty batch: valid, nothing to do

@@ -124,7 +124,8 @@ def test_align_walkthrough_on_gpu():
 @pytest.mark.parametrize("N,k,E,bm,dist", [
     (3, 2, 5, 16, "uniform"), (64, 8, 128, 16, "uniform"), (4096, 8, 128, 128, "uniform"),
     (16384, 8, 128, 128, "zipf"), (1000, 4, 7, 32, "one"), (333, 1, 1, 64, "uniform"),
-    (1, 8, 8, 16, "uniform"), (5000, 6, 512, 16, "zipf"), (777, 3, 60, 1, "uniform")])
+    (1, 8, 8, 16, "uniform"), (5000, 6, 512, 16, "zipf"), (777, 3, 60, 1, "uniform"),
+    (513, 8, 64, 16, "uniform"), (2048, 2, 3, 320, "one"), (9000, 4, 128, 320, "zipf")])
 def test_align_matches_oracle(N, k, E, bm, dist):
     rng = np.random.default_rng(N * 31 + E)
     if dist == "uniform":
@@ -157,7 +158,8 @@ SMALL = [
     random_case(70, 192, 9, 1, 64, dtype="bf16", seed=5, norm_topk_prob=False),  # k = 1
     random_case(40, 64, 1, 1, 128, dtype="bf16", seed=6),                      # E = 1: a dense SwiGLU
     random_case(300, 256, 32, 8, 128, dtype="bf16", seed=7, norm_topk_prob=False),
-    random_case(1500, 128, 8, 2, 64, dtype="bf16", seed=8),                    # block_m 128 path
+    random_case(1500, 128, 8, 2, 64, dtype="bf16", seed=8),                    # block_m 320 path
+    random_case(700, 128, 8, 2, 64, dtype="bf16", seed=15),                    # block_m 128 path
     random_case(600, 128, 16, 2, 64, dtype="bf16", seed=9),                    # block_m 64 path
     random_case(300, 128, 16, 2, 64, dtype="bf16", seed=10),                   # block_m 32 path
     random_case(2000, 320, 8, 2, 192, dtype="bf16", seed=13),                  # partial column tiles
