@@ -138,6 +138,7 @@ def bench_workload(name, steps, warmup, torch, moe):
         "cfg": cfg, "inputs": t, "ms_per_step": ms, "tokens_per_s": cfg.N / (ms * 1e-3),
         "tflops": cfg.flops() / (ms * 1e-3) / 1e12, "stage_ms": stage_ms, "work": work,
         "hit_experts": expert_hits(counts), "counts_min_max": [int(counts.min()), int(counts.max())],
+        "block_m": bm,
     }
     res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFLOPS
     weight_bytes = res["hit_experts"] * 3 * cfg.I * cfg.H * 2 + cfg.I_shared * 3 * cfg.H * 2
@@ -145,20 +146,59 @@ def bench_workload(name, steps, warmup, torch, moe):
     return res
 
 
+GEMM_SOURCES = ("sparse_moe_ffn_amd/csrc/grouped_gemm.hip", "sparse_moe_ffn_amd/csrc/moe_common.h",
+                "sparse_moe_ffn_amd/csrc/moe_launch.h")
+
+
+def gemm_source_hash():
+    """Hash of the GEMM sources with comments and blank space removed, so that
+    an edit of a comment keeps the committed counters valid and any change of
+    code voids them."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary (profiles/traffic_gate_up_<workload>.txt), or None when there is
+    none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != gemm_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
 def roofline_for(res):
     cfg = res["cfg"]
     kern = "gate_up"
     dur_s = res["stage_ms"][kern] * 1e-3
     w = res["work"][kern]
+    common = {"kernel": f"grouped_gemm_bf16 gate_up (SwiGLU epilogue), block_m {res['block_m']}",
+              "traffic": measured_traffic(cfg.name), "avg_launch_ms": round(res["stage_ms"][kern], 4)}
     if cfg.N * cfg.top_k / cfg.E < 64:          # few rows per expert: a weight stream
         achieved = w["bytes"] / dur_s / 1e9
-        return {"kernel": "grouped_gemm_bf16 gate_up (SwiGLU epilogue)", "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes_per_launch": w["bytes"], "avg_launch_ms": round(res["stage_ms"][kern], 4)}
+        return {**common, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": w["bytes"]}
     achieved = w["flops"] / dur_s / 1e12
-    return {"kernel": "grouped_gemm_bf16 gate_up (SwiGLU epilogue)", "bound": "mfma", "achieved": round(achieved, 1),
-            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None, "algorithmic_flops_per_launch": w["flops"], "avg_launch_ms": round(res["stage_ms"][kern], 4)}
+    return {**common, "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops_per_launch": w["flops"]}
 
 
 def cpu_baseline(res, budget_s, torch):

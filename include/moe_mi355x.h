@@ -99,8 +99,8 @@ int moe_get_workspace_layout(const moe_problem* p, moe_workspace_layout* layout)
 int moe_align_capacity(int64_t num_pairs, int64_t num_experts, int64_t block_m,
                        int64_t* max_rows, int64_t* max_tiles);
 
-/* Router (M03 题面速览, routing block; "Nano-vLLM 代码笔记 (八)",
- * Qwen3MoeSparseMoeBlock forward).
+/* Router (M03 题面速览, routing block; the nano-vLLM Qwen3-30B-A3B notes
+ * (lshu.cn/news/442807), qwen3_moe.py, Qwen3MoeSparseMoeBlock forward).
  *   x          [N, H]  dtype
  *   router_w   [E, H]  dtype
  *   shared_gate [H]    dtype or NULL; if given, shared_scale[n] =
@@ -167,7 +167,8 @@ int moe_gate_up(const moe_problem* p, const void* x, const void* w_gate_up,
                 int64_t block_m, int64_t max_tiles, void* act, void* stream);
 
 /* Grouped down product with the routing-weight epilogue (M03 题面速览;
- * "Nano-vLLM 代码笔记 (八)", the expert output times its routing weight):
+ * the nano-vLLM Qwen3-30B-A3B notes (lshu.cn/news/442807), qwen3_moe.py,
+ * Qwen3MoeSparseMoeBlock forward: the expert output times its routing weight):
  * for every tile row r holding pair p,
  *   y[p, h] = topk_w[p] * (act[r] . Wd[e, h]),
  *   w_down [E, H, I] dtype;  topk_w [N*k] float32;  y [N*k, H] dtype out,

@@ -11,7 +11,8 @@ Sources (the pages this follows, by title and section):
   sections "题面速览" (routing and block formula, the serving way, shared
   expert), "框架视角 · shape trace", "易错点", "逐步图：按 expert 分组的
   bookkeeping" (worked grouping and scalar examples), "三级提示" L1-L3.
-* [NANO] "Nano-vLLM 代码笔记 (八)", class ``Qwen3MoeSparseMoeBlock``
+* [NANO] the nano-vLLM Qwen3-30B-A3B notes at lshu.cn/news/442807,
+  qwen3_moe.py, class ``Qwen3MoeSparseMoeBlock``
   (router linear, float32 softmax, top-k, renormalisation, cast of the
   routing weights to the input dtype, one-hot expert mask, index_add_).
 * [Q35] "Qwen3.5 推理全流程", section 2.5B "Sparse MoE" (shared expert gated

@@ -8,8 +8,8 @@
 // formula, one product per expert over its gathered tokens) and L1 细节
 // (Wg, Wu are [I, H], Wd is [H, I]); the gate rows precede the up rows in the
 // packed gate/up weight.  The routing-weight multiply in the down epilogue is
-// the expert-output scaling of "Nano-vLLM 代码笔记 (八)",
-// Qwen3MoeSparseMoeBlock forward.
+// the expert-output scaling of the nano-vLLM Qwen3-30B-A3B notes
+// (lshu.cn/news/442807), qwen3_moe.py, Qwen3MoeSparseMoeBlock forward.
 //
 // Tiles come from the align kernel: tile t is rows [t*BM, (t+1)*BM) of the
 // padded pair list, all of one expert.  The launch covers an upper bound of

@@ -4,8 +4,8 @@
 // sigmoid(x . g) as one extra logit column.
 //
 // Follows "M03 · Sparse MoE：路由、按 expert 分组计算、shared expert",
-// 题面速览 (routing block) and "Nano-vLLM 代码笔记 (八)",
-// Qwen3MoeSparseMoeBlock forward.
+// 题面速览 (routing block) and the nano-vLLM Qwen3-30B-A3B notes
+// (lshu.cn/news/442807), qwen3_moe.py, Qwen3MoeSparseMoeBlock forward.
 //
 // Two kernels:
 //   logits: a (16-token tile) x (H slice) grid.  Each workgroup multiplies
