@@ -79,7 +79,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   else return row * BK + ((chunk ^ ((row >> 1) & 3)) << 3);
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int PFD, int MODE>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
   static_assert(BK == 32 || BK == 64, "stage depth");
   constexpr int kCpr = BK / 8;                      // 16-byte chunks per staged row
@@ -89,16 +89,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   constexpr int WN = BN / WAVES_N;
   constexpr int TM = WM / 16;
   constexpr int TN = WN / 16;
-  constexpr int ROWS = BM + BN;                     // staged rows: A tile, then B tile
-  constexpr int NDMA = ROWS / kRowsPerDma;          // wave DMAs per stage
-  constexpr int PER_WAVE = NDMA / NW;
+  constexpr int A_PER_WAVE = BM / kRowsPerDma / NW; // A-tile DMAs per stage and wave
+  constexpr int B_PER_WAVE = BN / kRowsPerDma / NW; // weight-tile DMAs per stage and wave
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(MODE != kGateUp || TN % 2 == 0, "gate/up needs matching gate and up sub-tiles");
-  static_assert(NDMA % NW == 0, "stage rows must split evenly over the waves");
-  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  static_assert(A_PER_WAVE * NW * kRowsPerDma == BM && B_PER_WAVE * NW * kRowsPerDma == BN,
+                "tile rows must split evenly over the waves' DMAs");
+  static_assert(SA >= 2 && SA <= 3 && SB >= SA && SB <= 6, "ring depths");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES][ROWS * BK];
-  __shared__ __attribute__((aligned(1024))) uint16_t pf_sink[kDmaBytes / 2];
+  // Two rings: SA stages of the A tile and SB > SA stages of the weight
+  // tile, in one LDS block (the epilogue reuses all of it).
+  constexpr int kAStage = BM * BK;                  // elements
+  constexpr int kBStage = BN * BK;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[SA * kAStage + SB * kBStage];
+  uint16_t* const ring_a = smem;
+  uint16_t* const ring_b = smem + SA * kAStage;
+  // Down: output row (pair index) and routing weight of every tile row,
+  // loaded once at the start so the epilogue reads them from LDS.
+  __shared__ int32_t ep_row[MODE == kDown ? BM : 1];
+  __shared__ float ep_scale[MODE == kDown ? BM : 1];
 
   const bool grouped = g.sorted_pairs != nullptr;
   const int half = BN / 2;
@@ -133,80 +142,72 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   const uint16_t* __restrict__ B = static_cast<const uint16_t*>(g.b) + (int64_t)expert * g.expert_stride;
   const int64_t b_rows = (MODE == kGateUp) ? 2 * (int64_t)g.n_out : g.n_out;
 
-  // Sources of this lane's 16-byte pieces: DMA q of this wave fills staged
-  // rows [8*gi, 8*gi + 8) with gi = wave + NW*q; lane i lands in row
-  // 8*gi + i/8, slot i%8, which holds chunk (i%8) ^ (row & 7).
-  const uint16_t* src[PER_WAVE];
+  // Sources of this lane's 16-byte pieces.  DMA q of this wave fills staged
+  // rows [R gi, R gi + R) of its ring stage, gi = wave + NW q, R rows per
+  // DMA; lane i lands in row R gi + i / kCpr, slot i % kCpr, which holds
+  // chunk swz^-1(slot) of that row.
+  const uint16_t* src_a[A_PER_WAVE];
+  const uint16_t* src_b[B_PER_WAVE];
 #pragma unroll
-  for (int q = 0; q < PER_WAVE; ++q) {
-    const int gi = wave + NW * q;
-    const int r = gi * kRowsPerDma + lane / kCpr;
-    const int slot = lane % kCpr;
-    const int chunk = (swz<BK>(r, slot) - r * BK) >> 3;   // the swizzle is its own inverse
-    const uint16_t* row_ptr;
-    if (r < BM) {
-      int64_t src_row;
-      if (MODE == kGateUp) {
-        if (grouped) {
-          const int pr = g.sorted_pairs[row0 + r];
-          src_row = (pr < g.num_pairs) ? pr / g.top_k : 0;     // sentinel rows read token 0
-        } else {
-          src_row = min(row0 + r, g.dense_rows - 1);
-        }
+  for (int q = 0; q < A_PER_WAVE; ++q) {
+    const int r = (wave + NW * q) * kRowsPerDma + lane / kCpr;
+    const int chunk = (swz<BK>(r, lane % kCpr) - r * BK) >> 3;   // the swizzle is its own inverse
+    int64_t src_row;
+    if (MODE == kGateUp) {
+      if (grouped) {
+        const int pr = g.sorted_pairs[row0 + r];
+        src_row = (pr < g.num_pairs) ? pr / g.top_k : 0;     // sentinel rows read token 0
       } else {
-        src_row = grouped ? (row0 + r) : min(row0 + r, g.dense_rows - 1);
+        src_row = min(row0 + r, g.dense_rows - 1);
       }
-      row_ptr = A + src_row * K;
     } else {
-      const int j = r - BM;
-      int64_t wrow;
-      if (MODE == kGateUp)
-        wrow = (j < half) ? (int64_t)nt * half + j : (int64_t)g.n_out + nt * half + (j - half);
-      else
-        wrow = (int64_t)nt * BN + j;
-      if (MODE == kGateUp) {                         // past the last column: reread a valid row
-        const int64_t lim = (j < half) ? g.n_out - 1 : b_rows - 1;
-        wrow = min(wrow, lim);
-      } else {
-        wrow = min(wrow, b_rows - 1);
-      }
-      row_ptr = B + wrow * K;
+      src_row = grouped ? (row0 + r) : min(row0 + r, g.dense_rows - 1);
     }
-    src[q] = row_ptr + chunk * 8;
+    src_a[q] = A + src_row * K + chunk * 8;
   }
-
-  // L2 warm-up (PFD > 0): with each stage's DMAs a wave also touches the
-  // cache lines of its share of the weight rows PFD stages further on, with
-  // one DMA into a scratch LDS line.  By the time that stage's real DMA runs,
-  // its weight lines are in L2, so the short LDS pipeline only has to cover
-  // L2 latency.  Every stage's DMAs are preceded by exactly one such touch,
-  // so the vmcnt arithmetic stays static.
-  constexpr int kPfRows = BN / NW;                   // weight rows per wave
-  constexpr int kPfLanesPerRow = 64 / kPfRows;       // lanes spread over each row's line
-  static_assert(PFD == 0 || (kPfRows >= 1 && kPfRows <= 64 && 64 % kPfRows == 0), "prefetch split");
-  const uint16_t* pf_src = nullptr;
-  if constexpr (PFD > 0) {
-    const int j = wave * kPfRows + (lane / kPfLanesPerRow);
+#pragma unroll
+  for (int q = 0; q < B_PER_WAVE; ++q) {
+    const int j = (wave + NW * q) * kRowsPerDma + lane / kCpr;
+    const int chunk = (swz<BK>(j, lane % kCpr) - j * BK) >> 3;
     int64_t wrow;
-    if (MODE == kGateUp)
+    if (MODE == kGateUp)                             // past the last column: reread a valid row
       wrow = (j < half) ? min((int64_t)nt * half + j, (int64_t)g.n_out - 1)
                         : min((int64_t)g.n_out + nt * half + (j - half), b_rows - 1);
     else
       wrow = min((int64_t)nt * BN + j, b_rows - 1);
-    pf_src = B + wrow * K + (lane % kPfLanesPerRow) * (BK / kPfLanesPerRow);
+    src_b[q] = B + wrow * K + chunk * 8;
   }
+
   const int nk = K / BK;
-  auto issue = [&](int kt, int st) {
-    if constexpr (PFD > 0) dma16(pf_src + min(kt + PFD, nk - 1) * BK, lds_addr(pf_sink));
+  auto issue_a = [&](int kt) {
+    const uint32_t base = lds_addr(ring_a + (kt % SA) * kAStage);
 #pragma unroll
-    for (int q = 0; q < PER_WAVE; ++q)
-      dma16(src[q] + kt * BK, lds_addr(&smem[st][(wave + NW * q) * kRowsPerDma * BK]));
+    for (int q = 0; q < A_PER_WAVE; ++q) dma16(src_a[q] + kt * BK, base + (wave + NW * q) * kDmaBytes);
   };
-  constexpr int kPerStage = PER_WAVE + (PFD > 0 ? 1 : 0);
-  auto wait_stage = [&](int ahead) {                 // ahead: stages issued past the current one
-    if (STAGES >= 4 && ahead >= 2) wait_vmcnt<((STAGES >= 4) ? 2 : 0) * kPerStage>();
-    else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<((STAGES >= 3) ? 1 : 0) * kPerStage>();
-    else wait_vmcnt<0>();
+  auto issue_b = [&](int kt) {
+    const uint32_t base = lds_addr(ring_b + (kt % SB) * kBStage);
+#pragma unroll
+    for (int q = 0; q < B_PER_WAVE; ++q) dma16(src_b[q] + kt * BK, base + (wave + NW * q) * kDmaBytes);
+  };
+  // Waits.  Each iteration issues the A DMAs of stage kt + SA - 1 and the
+  // weight DMAs of stage kt + SB - 1; with SB > SA the A DMAs go first, with
+  // SB == SA last, so either way a stage's A DMAs are issued no earlier than
+  // its weight DMAs.  Vector-memory loads complete in issue order, so once
+  // only the loads issued after stage kt's A DMAs are in flight, the whole
+  // stage has landed.  With SB > SA those are the weight DMAs of the same
+  // iteration plus SA - 2 whole iterations; with SB == SA, SA - 2 whole
+  // iterations.  The first SA - 1 stages come from the prologue (weights
+  // first, then A).  Near the end of the loop, where issues stop, and for
+  // short loops, the wait is for everything.
+  constexpr int a_ = A_PER_WAVE, b_ = B_PER_WAVE;
+  constexpr bool kAFirst = SB > SA;
+  constexpr int kSteady = (kAFirst ? b_ : 0) + (SA - 2) * (a_ + b_);
+  static_assert(kSteady < 64, "vmcnt range");
+  auto wait_stage = [&](int kt) {
+    if (nk < SB - 1 || kt + SB - 2 >= nk) { wait_vmcnt<0>(); return; }
+    if (kt >= SA - 1) { wait_vmcnt<kSteady>(); return; }
+    if (kt == 0) { wait_vmcnt<(SA - 2) * a_>(); return; }
+    wait_vmcnt<(SA >= 3 ? (SA - 3) * a_ + (a_ + b_) : 0)>();   // kt == 1 < SA - 1 (SA == 3)
   };
 
   floatx4 acc[TM][TN];
@@ -230,18 +231,38 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // The K loop.  Waves that hold only padding rows still issue their share
   // of the DMAs and take part in every barrier, but run a copy of the loop
   // without matrix work (choosing the copy outside the loop keeps both
-  // bodies branch-free, so the accumulators stay in AGPRs).
+  // bodies branch-free, so the accumulators stay put).
+  auto fill_tables = [&] {
+    if constexpr (MODE == kDown) {
+      for (int r = threadIdx.x; r < BM; r += 64 * NW) {
+        int prow = -1;
+        float sc = 0.0f;
+        if (r < rows_valid) {
+          prow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
+          sc = g.scale[prow];
+        }
+        ep_row[r] = prow;
+        ep_scale[r] = sc;
+      }
+    }
+  };
   auto main_loop = [&](auto compute) {
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue(s, s);
+    for (int s = 0; s < min(SB - 1, nk); ++s) issue_b(s);
+    for (int s = 0; s < min(SA - 1, nk); ++s) issue_a(s);
+    fill_tables();                                     // in the shadow of the first stage's loads
     for (int kt = 0; kt < nk; ++kt) {
-      wait_stage(min(nk - 1 - kt, STAGES - 2));
+      wait_stage(kt);
       __syncthreads();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      if constexpr (kAFirst) {
+        if (kt + SA - 1 < nk) issue_a(kt + SA - 1);
+        if (kt + SB - 1 < nk) issue_b(kt + SB - 1);
+      } else {
+        if (kt + SB - 1 < nk) issue_b(kt + SB - 1);
+        if (kt + SA - 1 < nk) issue_a(kt + SA - 1);
+      }
       if constexpr (decltype(compute)::value) {
-        const uint16_t* As = smem[kt % STAGES];
-        const uint16_t* Bs = As + BM * BK;
+        const uint16_t* As = ring_a + (kt % SA) * kAStage;
+        const uint16_t* Bs = ring_b + (kt % SB) * kBStage;
 #pragma unroll
         for (int kk = 0; kk < BK / 32; ++kk) {
           const int ch = kk * 4 + (lane >> 4);
@@ -269,8 +290,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // row operand, so lane l holds output columns 4*(l/16) .. +3 of row l%16 of
   // each 16x16 sub-tile.  The tile is finished in registers (SwiGLU, or the
   // routing weight), packed to bf16 four columns at a time into LDS (the
-  // pipeline buffers are free now), then written out as whole rows with
-  // 16-byte stores.
+  // rings are free now), then written out as whole rows with 16-byte stores.
   constexpr int OUT_COLS = (MODE == kGateUp) ? BN / 2 : BN;
   constexpr int OUT_LD = OUT_COLS + 8;                 // staged row pitch (+16 B against bank conflicts)
   // Rows staged per pass: whole wave rows, as many as fit in the LDS.
@@ -279,7 +299,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   static_assert(EPI_ROWS >= WM, "one wave row of the output tile must fit the LDS");
   constexpr int kThreads = 64 * NW;
   constexpr int CPR = OUT_COLS / 8;                    // 16-byte chunks per output row
-  uint16_t* so = &smem[0][0];
+  uint16_t* so = smem;
   const int col0 = (MODE == kGateUp) ? nt * half : nt * BN;
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   for (int e0 = 0; e0 < BM; e0 += EPI_ROWS) {
@@ -290,11 +310,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
       for (int tm = 0; tm < TM; ++tm) {
         const int m = wm * WM + tm * 16 + (lane & 15);
         const int ml = m - e0;
-        float sc = 1.0f;
-        if (MODE == kDown) {
-          const int prow = (m < rows_valid) ? (grouped ? g.sorted_pairs[row0 + m] : row0 + m) : -1;
-          sc = (prow >= 0) ? g.scale[prow] : 0.0f;
-        }
+        const float sc = (MODE == kDown) ? ep_scale[m] : 1.0f;
         if (MODE == kGateUp) {
           constexpr int kHalfTN = TN / 2;
 #pragma unroll
@@ -302,7 +318,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
             const int n = wn * (WN / 2) + t * 16 + (lane >> 4) * 4;
             float v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = silu_f32(acc[tm][t][i]) * acc[tm][t + kHalfTN][i];
+            for (int i = 0; i < 4; ++i) v[i] = silu_fast(acc[tm][t][i]) * acc[tm][t + kHalfTN][i];
             *reinterpret_cast<uint2*>(so + ml * OUT_LD + n) =
                 uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
@@ -323,9 +339,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
       const int rl = c / CPR, j = c % CPR;
       if (col0 + j * 8 >= g.n_out) continue;
       const int r = e0 + rl;
-      int64_t orow;
-      if (MODE == kGateUp) orow = row0 + r;
-      else orow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
+      const int64_t orow = (MODE == kGateUp) ? row0 + r : ep_row[r];
       *reinterpret_cast<uint4*>(C + orow * g.n_out + col0 + j * 8) =
           *reinterpret_cast<const uint4*>(so + rl * OUT_LD + j * 8);
     }
@@ -384,13 +398,13 @@ __global__ __launch_bounds__(kF32Threads) void grouped_gemm_f32_kernel(GemmProbl
 
 // ---------------------------------------------------------------- launchers
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int STAGES, int PFD, int MODE>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE>
 static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
   if (g.block_m != BM) return hipErrorInvalidValue;   // tiles must be laid out for this height
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
   const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, STAGES, PFD, MODE>),
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE>),
                      dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
   return hipGetLastError();
 }
@@ -404,11 +418,11 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     return hipGetLastError();
   }
   switch (g.block_m) {
-    case 16: return launch_bf16<16, 128, 64, 1, 2, 4, 0, MODE>(g, s);
-    case 32: return launch_bf16<32, 128, 64, 1, 4, 4, 0, MODE>(g, s);
-    case 64: return launch_bf16<64, 256, 64, 1, 4, 3, 0, MODE>(g, s);
-    case 128: return launch_bf16<128, 256, 64, 2, 4, 3, 0, MODE>(g, s);
-    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 0, MODE>(g, s);
+    case 16: return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, s);
+    case 32: return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, s);
+    case 64: return launch_bf16<64, 256, 64, 1, 4, 2, 3, MODE>(g, s);
+    case 128: return launch_bf16<128, 256, 64, 2, 4, 2, 3, MODE>(g, s);
+    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
