@@ -79,6 +79,8 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   else return row * BK + ((chunk ^ ((row >> 1) & 3)) << 3);
 }
 
+constexpr bool kRotateK = true;
+
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
   static_assert(BK == 32 || BK == 64, "stage depth");
@@ -179,15 +181,26 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   }
 
   const int nk = K / BK;
+  // The K loop starts at stage kstart and wraps around.  Rows of 2^n bytes
+  // put every stage-kt load of every workgroup on the same low address bits,
+  // and so on the same few HBM channels, if all workgroups walk K in step;
+  // rotating the start by expert spreads them, while the column blocks of
+  // one expert stay in step and keep sharing its A rows in L2.  The start
+  // depends only on the expert, so every output element keeps one
+  // summation order whatever the batch.
+  const int kstart = (kRotateK ? expert * 7 : 0) % nk;
+  auto kpos = [&](int kt) { const int k = kt + kstart; return (k >= nk ? k - nk : k) * BK; };
   auto issue_a = [&](int kt) {
     const uint32_t base = lds_addr(ring_a + (kt % SA) * kAStage);
+    const int ko = kpos(kt);
 #pragma unroll
-    for (int q = 0; q < A_PER_WAVE; ++q) dma16(src_a[q] + kt * BK, base + (wave + NW * q) * kDmaBytes);
+    for (int q = 0; q < A_PER_WAVE; ++q) dma16(src_a[q] + ko, base + (wave + NW * q) * kDmaBytes);
   };
   auto issue_b = [&](int kt) {
     const uint32_t base = lds_addr(ring_b + (kt % SB) * kBStage);
+    const int ko = kpos(kt);
 #pragma unroll
-    for (int q = 0; q < B_PER_WAVE; ++q) dma16(src_b[q] + kt * BK, base + (wave + NW * q) * kDmaBytes);
+    for (int q = 0; q < B_PER_WAVE; ++q) dma16(src_b[q] + ko, base + (wave + NW * q) * kDmaBytes);
   };
   // Waits.  Each iteration issues the A DMAs of stage kt + SA - 1 and the
   // weight DMAs of stage kt + SB - 1; with SB > SA the A DMAs go first, with
