@@ -229,8 +229,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // 16-row sub-tiles of this wave that hold real rows (the rest is padding).
-  const int tm_valid = min(TM, max(0, (rows_valid - wm * WM + 15) / 16));
+  // Row groups: the tile's 16-row groups are dealt to the wave rows in turn
+  // (group wm + WAVES_M tm is this wave's tm-th), so the padding at the end
+  // of a tile is spread over all waves.  Each wave computes only its groups
+  // that hold real rows.
+  auto group_row = [&](int tm) { return 16 * (wm + WAVES_M * tm); };
+  const int groups_valid = (rows_valid + 15) / 16;
+  const int tm_valid = min(TM, (max(0, groups_valid - wm) + WAVES_M - 1) / WAVES_M);
 
   auto b_tile_row = [&](int tn) {
     if (MODE == kGateUp) {
@@ -241,10 +246,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
     return wn * WN + tn * 16 + (lane & 15);
   };
 
-  // The K loop.  Waves that hold only padding rows still issue their share
-  // of the DMAs and take part in every barrier, but run a copy of the loop
-  // without matrix work (choosing the copy outside the loop keeps both
-  // bodies branch-free, so the accumulators stay put).
+  // The K loop, in one copy per count of real row groups (chosen outside the
+  // loop, so every body is branch-free and the accumulators stay put).
+  // Waves with no real rows still issue their share of the DMAs and take
+  // part in every barrier.
   auto fill_tables = [&] {
     if constexpr (MODE == kDown) {
       for (int r = threadIdx.x; r < BM; r += 64 * NW) {
@@ -273,31 +278,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
         if (kt + SB - 1 < nk) issue_b(kt + SB - 1);
         if (kt + SA - 1 < nk) issue_a(kt + SA - 1);
       }
-      if constexpr (decltype(compute)::value) {
+      constexpr int TMV = decltype(compute)::value;
+      if constexpr (TMV > 0) {
         const uint16_t* As = ring_a + (kt % SA) * kAStage;
         const uint16_t* Bs = ring_b + (kt % SB) * kBStage;
 #pragma unroll
         for (int kk = 0; kk < BK / 32; ++kk) {
           const int ch = kk * 4 + (lane >> 4);
-          uint4 af[TM], bfr[TN];
+          uint4 af[TMV], bfr[TN];
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn)
             bfr[tn] = *reinterpret_cast<const uint4*>(Bs + swz<BK>(b_tile_row(tn), ch));
 #pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
-            af[tm] = *reinterpret_cast<const uint4*>(As + swz<BK>(wm * WM + tm * 16 + (lane & 15), ch));
+          for (int tm = 0; tm < TMV; ++tm)
+            af[tm] = *reinterpret_cast<const uint4*>(As + swz<BK>(group_row(tm) + (lane & 15), ch));
 #pragma unroll
-          for (int tm = 0; tm < TM; ++tm)
+          for (int tm = 0; tm < TMV; ++tm)
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = mfma16x16x32(bfr[tn], af[tm], acc[tm][tn]);
         }
       }
     }
   };
-  if (tm_valid > 0)
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
+  static_assert(TM <= 5, "the row-group dispatch covers TM <= 5");
+  switch (tm_valid) {
+    case 0: main_loop(std::integral_constant<int, 0>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (TM >= 2) main_loop(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (TM >= 3) main_loop(std::integral_constant<int, 3>{}); break;
+    case 4: if constexpr (TM >= 4) main_loop(std::integral_constant<int, 4>{}); break;
+    default: if constexpr (TM >= 5) main_loop(std::integral_constant<int, 5>{}); break;
+  }
 
   // Epilogue.  The products were taken with the weight fragment as the MFMA's
   // row operand, so lane l holds output columns 4*(l/16) .. +3 of row l%16 of
@@ -306,10 +317,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // rings are free now), then written out as whole rows with 16-byte stores.
   constexpr int OUT_COLS = (MODE == kGateUp) ? BN / 2 : BN;
   constexpr int OUT_LD = OUT_COLS + 8;                 // staged row pitch (+16 B against bank conflicts)
-  // Rows staged per pass: whole wave rows, as many as fit in the LDS.
+  // Rows staged per pass: whole row groups, as many as fit in the LDS.
   constexpr int kFitRows = (int)sizeof(smem) / (OUT_LD * 2);
-  constexpr int EPI_ROWS = (kFitRows >= BM) ? BM : (kFitRows / WM) * WM;
-  static_assert(EPI_ROWS >= WM, "one wave row of the output tile must fit the LDS");
+  constexpr int EPI_ROWS = (kFitRows >= BM) ? BM : (kFitRows / 16) * 16;
+  static_assert(EPI_ROWS >= 16, "one row group of the output tile must fit the LDS");
   constexpr int kThreads = 64 * NW;
   constexpr int CPR = OUT_COLS / 8;                    // 16-byte chunks per output row
   uint16_t* so = smem;
@@ -317,11 +328,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   uint16_t* __restrict__ C = static_cast<uint16_t*>(g.c);
   for (int e0 = 0; e0 < BM; e0 += EPI_ROWS) {
     __syncthreads();                                   // LDS free: last stage or last pass consumed
-    const bool mine = tm_valid > 0 && wm * WM >= e0 && wm * WM < e0 + EPI_ROWS;
-    if (mine) {
+    {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        const int m = wm * WM + tm * 16 + (lane & 15);
+        if (tm >= tm_valid || group_row(tm) < e0 || group_row(tm) >= e0 + EPI_ROWS) continue;
+        const int m = group_row(tm) + (lane & 15);
         const int ml = m - e0;
         const float sc = (MODE == kDown) ? ep_scale[m] : 1.0f;
         if (MODE == kGateUp) {
