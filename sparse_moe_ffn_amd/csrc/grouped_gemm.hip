@@ -91,13 +91,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   constexpr int WN = BN / WAVES_N;
   constexpr int TM = WM / 16;
   constexpr int TN = WN / 16;
-  constexpr int A_PER_WAVE = BM / kRowsPerDma / NW; // A-tile DMAs per stage and wave
-  constexpr int B_PER_WAVE = BN / kRowsPerDma / NW; // weight-tile DMAs per stage and wave
+  // Wave-wide DMAs per stage: NA_DMA for the A tile, NB_DMA for the weight
+  // tile.  DMA gi goes to wave gi % NW, so waves below the remainder issue
+  // one more than the others.
+  constexpr int NA_DMA = BM / kRowsPerDma, NB_DMA = BN / kRowsPerDma;
+  constexpr int kAFull = NA_DMA / NW, kARem = NA_DMA % NW;
+  constexpr int kBFull = NB_DMA / NW, kBRem = NB_DMA % NW;
+  constexpr int A_PER_WAVE = kAFull + (kARem ? 1 : 0);
+  constexpr int B_PER_WAVE = kBFull + (kBRem ? 1 : 0);
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(MODE != kGateUp || TN % 2 == 0, "gate/up needs matching gate and up sub-tiles");
-  static_assert(A_PER_WAVE * NW * kRowsPerDma == BM && B_PER_WAVE * NW * kRowsPerDma == BN,
-                "tile rows must split evenly over the waves' DMAs");
-  static_assert(SA >= 2 && SA <= 3 && SB >= SA && SB <= 6, "ring depths");
+  static_assert(NA_DMA * kRowsPerDma == BM && NB_DMA * kRowsPerDma == BN,
+                "tile rows must fill whole DMAs");
+  static_assert(SA >= 2 && SA <= 5 && SB >= SA && SB <= 6, "ring depths");
 
   // Two rings: SA stages of the A tile and SB > SA stages of the weight
   // tile, in one LDS block (the epilogue reuses all of it).
@@ -152,6 +158,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   const uint16_t* src_b[B_PER_WAVE];
 #pragma unroll
   for (int q = 0; q < A_PER_WAVE; ++q) {
+    src_a[q] = A;
+    if (wave + NW * q >= NA_DMA) continue;             // this wave has no DMA q
     const int r = (wave + NW * q) * kRowsPerDma + lane / kCpr;
     const int chunk = (swz<BK>(r, lane % kCpr) - r * BK) >> 3;   // the swizzle is its own inverse
     int64_t src_row;
@@ -169,6 +177,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   }
 #pragma unroll
   for (int q = 0; q < B_PER_WAVE; ++q) {
+    src_b[q] = B;
+    if (wave + NW * q >= NB_DMA) continue;
     const int j = (wave + NW * q) * kRowsPerDma + lane / kCpr;
     const int chunk = (swz<BK>(j, lane % kCpr) - j * BK) >> 3;
     int64_t wrow;
@@ -194,13 +204,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
     const uint32_t base = lds_addr(ring_a + (kt % SA) * kAStage);
     const int ko = kpos(kt);
 #pragma unroll
-    for (int q = 0; q < A_PER_WAVE; ++q) dma16(src_a[q] + ko, base + (wave + NW * q) * kDmaBytes);
+    for (int q = 0; q < A_PER_WAVE; ++q)
+      if (q < kAFull || wave < kARem) dma16(src_a[q] + ko, base + (wave + NW * q) * kDmaBytes);
   };
   auto issue_b = [&](int kt) {
     const uint32_t base = lds_addr(ring_b + (kt % SB) * kBStage);
     const int ko = kpos(kt);
 #pragma unroll
-    for (int q = 0; q < B_PER_WAVE; ++q) dma16(src_b[q] + ko, base + (wave + NW * q) * kDmaBytes);
+    for (int q = 0; q < B_PER_WAVE; ++q)
+      if (q < kBFull || wave < kBRem) dma16(src_b[q] + ko, base + (wave + NW * q) * kDmaBytes);
   };
   // Waits.  Each iteration issues the A DMAs of stage kt + SA - 1 and the
   // weight DMAs of stage kt + SB - 1; with SB > SA the A DMAs go first, with
@@ -212,15 +224,36 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // iterations.  The first SA - 1 stages come from the prologue (weights
   // first, then A).  Near the end of the loop, where issues stop, and for
   // short loops, the wait is for everything.
-  constexpr int a_ = A_PER_WAVE, b_ = B_PER_WAVE;
+  // The counts below are this wave's DMAs per stage (a_ for A, b_ for the
+  // weights), which differ between waves when the DMAs do not split evenly.
   constexpr bool kAFirst = SB > SA;
-  constexpr int kSteady = (kAFirst ? b_ : 0) + (SA - 2) * (a_ + b_);
-  static_assert(kSteady < 64, "vmcnt range");
-  auto wait_stage = [&](int kt) {
+  static_assert((kAFirst ? B_PER_WAVE : 0) + (SA - 2) * (A_PER_WAVE + B_PER_WAVE) < 64, "vmcnt range");
+  auto wait_counts = [&](int kt, auto a_tag, auto b_tag) {
+    constexpr int a_ = decltype(a_tag)::value, b_ = decltype(b_tag)::value;
+    constexpr int kSteady = (kAFirst ? b_ : 0) + (SA - 2) * (a_ + b_);
     if (nk < SB - 1 || kt + SB - 2 >= nk) { wait_vmcnt<0>(); return; }
     if (kt >= SA - 1) { wait_vmcnt<kSteady>(); return; }
-    if (kt == 0) { wait_vmcnt<(SA - 2) * a_>(); return; }
-    wait_vmcnt<(SA >= 3 ? (SA - 3) * a_ + (a_ + b_) : 0)>();   // kt == 1 < SA - 1 (SA == 3)
+    // kt < SA - 1: stage kt's A DMAs came from the prologue, followed there by
+    // those of stages kt+1 .. SA-2 and then by kt whole iterations.
+    auto early = [&](auto k_tag) {
+      constexpr int k = decltype(k_tag)::value;
+      wait_vmcnt<(SA - 2 - k) * a_ + k * (a_ + b_)>();
+    };
+    if (kt == 0) early(std::integral_constant<int, 0>{});
+    else if (kt == 1) early(std::integral_constant<int, (SA > 2 ? 1 : 0)>{});
+    else if (kt == 2) early(std::integral_constant<int, (SA > 3 ? 2 : 0)>{});
+    else early(std::integral_constant<int, (SA > 4 ? 3 : 0)>{});
+  };
+  auto wait_stage = [&](int kt) {
+    using AF = std::integral_constant<int, kAFull>;
+    using AX = std::integral_constant<int, kAFull + 1>;
+    using BF = std::integral_constant<int, kBFull>;
+    using BX = std::integral_constant<int, kBFull + 1>;
+    const bool ax = wave < kARem, bx = wave < kBRem;
+    if (ax && bx) wait_counts(kt, AX{}, BX{});
+    else if (ax) wait_counts(kt, AX{}, BF{});
+    else if (bx) wait_counts(kt, AF{}, BX{});
+    else wait_counts(kt, AF{}, BF{});
   };
 
   floatx4 acc[TM][TN];
