@@ -238,32 +238,77 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_bf16_kernel(
     for (int t = 0; t < TT; ++t) acc[t][i] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const uint4 zero = {0u, 0u, 0u, 0u};
-  constexpr int kUnroll = (TT == 1) ? 4 : 2;
-  for (int s0 = kb; s0 < ke; s0 += kUnroll) {
-    uint4 a[kUnroll][TT];
-    uint4 b[kUnroll][SUBW];
+  if constexpr (TT == 1) {
+    constexpr int kUnroll = 4;
+    for (int s0 = kb; s0 < ke; s0 += kUnroll) {
+      uint4 a[kUnroll][TT];
+      uint4 b[kUnroll][SUBW];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (s0 + u < ke) {
-        const int k0 = (s0 + u) * 32;
+      for (int u = 0; u < kUnroll; ++u) {
+        if (s0 + u < ke) {
+          const int k0 = (s0 + u) * 32;
 #pragma unroll
-        for (int t = 0; t < TT; ++t) a[u][t] = *reinterpret_cast<const uint4*>(a_src[t] + k0);
+          for (int t = 0; t < TT; ++t) a[u][t] = *reinterpret_cast<const uint4*>(a_src[t] + k0);
 #pragma unroll
-        for (int i = 0; i < SUBW; ++i)
-          if (wave + kLogitsWaves * i < nsub)
-            b[u][i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
+          for (int i = 0; i < SUBW; ++i)
+            if (wave + kLogitsWaves * i < nsub)
+              b[u][i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if (s0 + u < ke) {
+#pragma unroll
+          for (int i = 0; i < SUBW; ++i)
+            if (wave + kLogitsWaves * i < nsub) {
+#pragma unroll
+              for (int t = 0; t < TT; ++t) acc[t][i] = mfma16x16x32(a[u][t], b[u][i], acc[t][i]);
+            }
+        }
       }
     }
+  } else {
+    // TT token tiles: wave w < TT loads the fragments of tile w for a chunk
+    // of k-steps into LDS (in fragment order: lane-linear 1 KB blocks, so the
+    // reads are conflict-free), and every wave multiplies all TT tiles with
+    // its router fragments.  Each x fragment is loaded from memory once per
+    // workgroup instead of once per wave.  The k-steps are still taken in
+    // order, so every logit is summed exactly as in the TT = 1 path.
+    static_assert(TT <= kLogitsWaves, "one loading wave per token tile");
+    constexpr int kChunk = (SUBW <= 3) ? 8 : 2;       // k-steps per LDS round (register budget)
+    __shared__ uint4 a_lds[TT][kChunk][kWave];
+    const uint16_t* my_a = x + (int64_t)min(t0 + wave * 16 + (lane & 15), N - 1) * H + (lane >> 4) * 8;
+    for (int s0 = kb; s0 < ke; s0 += kChunk) {
+      const int ns = min(kChunk, ke - s0);
+      // Steps past the slice end reload its last step (in bounds, never used).
+      if (wave < TT) {
+        uint4 a[kChunk];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (s0 + u < ke) {
+        for (int u = 0; u < kChunk; ++u) a[u] = *reinterpret_cast<const uint4*>(my_a + min(s0 + u, ke - 1) * 32);
 #pragma unroll
-        for (int i = 0; i < SUBW; ++i)
-          if (wave + kLogitsWaves * i < nsub) {
-#pragma unroll
-            for (int t = 0; t < TT; ++t) acc[t][i] = mfma16x16x32(a[u][t], b[u][i], acc[t][i]);
-          }
+        for (int u = 0; u < kChunk; ++u) a_lds[wave][u][lane] = a[u];
       }
+      uint4 b[kChunk][SUBW];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int k0 = min(s0 + u, ke - 1) * 32;
+#pragma unroll
+        for (int i = 0; i < SUBW; ++i) b[u][i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        if (u < ns) {
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            const uint4 af = a_lds[t][u][lane];
+#pragma unroll
+            for (int i = 0; i < SUBW; ++i)
+              if (wave + kLogitsWaves * i < nsub) acc[t][i] = mfma16x16x32(af, b[u][i], acc[t][i]);
+          }
+        }
+      }
+      __syncthreads();
     }
   }
   float* dst = partial + (int64_t)blockIdx.y * N * cols;
