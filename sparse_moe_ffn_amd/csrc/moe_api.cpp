@@ -87,6 +87,17 @@ int64_t choose_block_m(const moe_problem* p) {
   return 320;                       // one tile holds a typical prefill expert
 }
 
+// Row-tile height of the dense shared-expert products: tall tiles (fewer
+// bytes per flop) once there are enough rows to fill the GPU with them.
+int64_t shared_block_m(const moe_problem* p) {
+  if (p->dtype == MOE_F32) return 16;
+  const int64_t N = p->num_tokens;
+  if (N >= 4096) return 320;
+  if (N >= 512) return 128;
+  if (N >= 128) return 64;
+  return 16;
+}
+
 bool block_m_supported(int32_t dtype, int64_t bm) {
   if (dtype == MOE_F32) return bm >= 1 && bm <= 1024;
   return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 320;
@@ -287,7 +298,7 @@ int moe_shared_expert(const moe_problem* p, const void* x, const void* shared_w_
     return fail(MOE_EINVAL, "NULL tensor");
   if (int rc = check_ptrs_bf16(p, {x, shared_w_gate_up, shared_w_down, shared_act, shared_y})) return rc;
   const int64_t N = p->num_tokens;
-  const int64_t bm = p->dtype == MOE_F32 ? 16 : 128;
+  const int64_t bm = shared_block_m(p);
   moe::GemmProblem g = gemm_common(p);
   g.dense_rows = (int32_t)N;
   g.block_m = (int32_t)bm;
