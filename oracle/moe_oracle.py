@@ -3,7 +3,8 @@
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
 leg of the benchmark may import this module; the product path never does.  It
 shares no code with the GPU library (it imports numpy and the standard library
-only) and is deliberately plain and slow.
+only, plus torch's float32-to-bfloat16 conversion where a value is rounded
+to the activation dtype) and is deliberately plain and slow.
 
 Sources (the pages this follows, by title and section):
 
@@ -16,7 +17,9 @@ Sources (the pages this follows, by title and section):
   (router linear, float32 softmax, top-k, renormalisation, cast of the
   routing weights to the input dtype, one-hot expert mask, index_add_).
 * [Q35] "Qwen3.5 推理全流程", section 2.5B "Sparse MoE" (shared expert gated
-  by a sigmoid of a per-token scalar).
+  by a sigmoid of a per-token scalar) and 2.5A "Dense MLP".
+* [STEP19] "Step 19: Real Model — Qwen3ForCausalLM", section "RMSNorm：去掉
+  均值中心化" (the RMSNorm formula in front of the MLP).
 
 Precision.  The pages fix the routing precision: probabilities come from a
 float32 softmax over all E experts and renormalisation is done in float32
@@ -304,6 +307,63 @@ def moe_forward_masked(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, sh
         for n in range(N):
             out[n] += shared_term(x[n], shared)
     return out
+
+
+# --------------------------------------------------------------------------
+# Dense SwiGLU layer ("Qwen3.5 推理全流程" 2.5A Dense MLP; [NANO] the
+# Qwen3MLP / Qwen3MoeMLP used for the layers listed in mlp_only_layers or
+# skipped by decoder_sparse_step): the expert formula applied to every token,
+# with no router and no weight -- the E = k = 1 case of the block.
+# --------------------------------------------------------------------------
+
+def dense_mlp(x, w_gate_up, w_down):
+    """(silu(x Wg^T) * (x Wu^T)) Wd^T for every row of x, float64; w_gate_up
+    is [2I, H] with the gate rows first, w_down is [H, I]."""
+    gu = np.asarray(w_gate_up, dtype=F64)
+    I = gu.shape[0] // 2
+    return swiglu(x, gu[:I], gu[I:], w_down)
+
+
+# --------------------------------------------------------------------------
+# Residual add + RMSNorm in front of the block.  [NANO] Qwen3DecoderLayer
+# and question 4 of the notes: the layer norm before the MLP is called with
+# the residual stream -- the incoming activations are added to it, the sum
+# is the new residual, and its normalisation is what the MLP (here the MoE
+# block) reads; with no residual yet (first layer) the input itself is the
+# residual.  "Step 19: Real Model — Qwen3ForCausalLM", section "RMSNorm：去掉
+# 均值中心化": RMSNorm(h) = h / sqrt(mean(h^2) + eps) * weight, no mean
+# subtraction and no bias.  [M08] 细节: the residual carries the
+# un-normalised sum.
+# --------------------------------------------------------------------------
+
+def rms_norm(h, weight, eps: float):
+    """h / sqrt(mean(h^2 over the last axis) + eps) * weight, float64."""
+    h = np.asarray(h, dtype=F64)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return h / np.sqrt(ms + eps) * np.asarray(weight, dtype=F64)
+
+
+def round_to(a, dtype: str) -> np.ndarray:
+    """Round float32 values to the activation dtype ("bf16": round to nearest
+    even, the rounding of a stored bfloat16 tensor; "f32": unchanged)."""
+    a = np.asarray(a, dtype=F32)
+    if dtype == "f32":
+        return a
+    import torch  # dtype conversion only (a library primitive)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).float().numpy()
+
+
+def add_rmsnorm(x, residual, weight, eps: float, dtype: str):
+    """(normed float64, new residual float32 holding dtype values).
+
+    The new residual is x + residual (x alone when residual is None), added
+    in float32 and rounded once to the activation dtype -- the value a
+    caller stores; normed is the RMSNorm of that stored residual."""
+    h = np.asarray(x, dtype=F32)
+    if residual is not None:
+        h = (h + np.asarray(residual, dtype=F32)).astype(F32)
+    r = round_to(h, dtype)
+    return rms_norm(r, weight, eps), r
 
 
 def tolerance(ref: np.ndarray, dtype: str) -> float:

@@ -420,3 +420,95 @@ def test_tolerance_formula():
     ref = np.array([[0.5, -2.0]])
     assert O.tolerance(ref, "bf16") == pytest.approx(2e-2 * 2.0 + 1e-3)
     assert O.tolerance(ref, "f32") == pytest.approx(1e-4 * 2.0)
+
+
+# ----------------------------------------------------- dense SwiGLU layer
+
+def test_dense_mlp_matches_page_expert_table():
+    """Each expert of the page's scalar example, run as a dense layer over the
+    two tokens, gives the page's per-expert outputs."""
+    g = golden("m03_scalar_block.json")
+    _, gu, wd = scalar_weights(g)
+    x = np.array([[2.0], [-1.0]])
+    for e in range(g["E"]):
+        y = O.dense_mlp(x, gu[e], wd[e])[:, 0]
+        assert rnd(y, g["decimals"]) == [g["per_expert_out"]["x=2"][e], g["per_expert_out"]["x=-1"][e]]
+
+
+def test_dense_mlp_matches_torch_and_one_expert_block():
+    rng = np.random.default_rng(21)
+    x, r, gu, wd, _ = rand_case(rng, 7, 16, 1, 1, 24)
+    d = O.dense_mlp(x, gu[0], wd[0])
+    xt, gt = torch.from_numpy(x).double(), torch.from_numpy(gu[0]).double()
+    F = torch.nn.functional
+    ref = F.linear(F.silu(F.linear(xt, gt[:24])) * F.linear(xt, gt[24:]), torch.from_numpy(wd[0]).double())
+    np.testing.assert_allclose(d, ref.numpy(), rtol=1e-12, atol=1e-12)
+    out, _ = O.moe_forward(x, r, gu, wd, 1, False)
+    np.testing.assert_allclose(out, d, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------- residual add + RMSNorm
+
+def test_round_to_bf16_nearest_even():
+    # bf16 keeps 7 fraction bits: 1 + 2^-8 is halfway to 1 + 2^-7 and goes to
+    # the even neighbour 1; 1 + 3*2^-8 is halfway between 1 + 2^-7 (odd) and
+    # 1 + 2^-6 (even).
+    v = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 3.0], np.float32)
+    np.testing.assert_array_equal(O.round_to(v, "bf16"), [1.0, 1 + 2.0 ** -6, -1.0, 3.0])
+    np.testing.assert_array_equal(O.round_to(v, "f32"), v)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 1e-2, 0.5])
+def test_rms_norm_matches_torch(eps):
+    rng = np.random.default_rng(22)
+    h = rng.standard_normal((6, 40)) * 3
+    w = rng.standard_normal(40)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(h), (40,), torch.from_numpy(w), eps)
+    np.testing.assert_allclose(O.rms_norm(h, w, eps), ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_rms_norm_closed_forms():
+    H = 16
+    ones = np.ones(H)
+    for c in (2.0, -0.5, 1e-3):                  # constant row: c / sqrt(c^2 + eps)
+        np.testing.assert_allclose(O.rms_norm(np.full(H, c), ones, 1e-6), c / np.sqrt(c * c + 1e-6), rtol=1e-14)
+    rng = np.random.default_rng(23)
+    h = rng.standard_normal((5, H))
+    y = O.rms_norm(h, ones, 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-12)     # unit RMS
+    np.testing.assert_allclose(O.rms_norm(7.5 * h, ones, 0.0), y, rtol=1e-12)  # scale invariant
+    np.testing.assert_allclose(O.rms_norm(h, 3 * ones, 0.0), 3 * y, rtol=1e-12)
+
+
+def test_add_rmsnorm_residual_semantics():
+    rng = np.random.default_rng(24)
+    x = O.round_to(rng.standard_normal((4, 32)), "bf16")
+    res = O.round_to(rng.standard_normal((4, 32)) * 4, "bf16")
+    w = rng.standard_normal(32)
+    # first layer: the input is the residual
+    n0, r0 = O.add_rmsnorm(x, None, w, 1e-6, "bf16")
+    np.testing.assert_array_equal(r0, x)
+    # later layers: the residual carries the un-normalised float32 sum
+    n1, r1 = O.add_rmsnorm(x, res, w, 1e-6, "bf16")
+    s = torch.from_numpy(x) + torch.from_numpy(res)
+    np.testing.assert_array_equal(r1, s.to(torch.bfloat16).float().numpy())
+    for n, r in ((n0, r0), (n1, r1)):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(r).double(), (32,), torch.from_numpy(w), 1e-6)
+        np.testing.assert_allclose(n, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_add_rmsnorm_pin_catches_norm_before_add(monkeypatch):
+    """Planted mistake: normalising the input before adding the residual."""
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((3, 16)).astype(np.float32)
+    res = (rng.standard_normal((3, 16)) * 4).astype(np.float32)
+    w = np.ones(16)
+
+    def wrong(x_, residual, weight, eps, dtype):
+        n = O.rms_norm(x_, weight, eps)
+        r = O.round_to((n + residual).astype(np.float32), dtype)
+        return O.rms_norm(r, weight, eps), r
+
+    monkeypatch.setattr(O, "add_rmsnorm", wrong)
+    _, r = O.add_rmsnorm(x, res, w, 1e-6, "f32")
+    assert not np.array_equal(r, (x + res).astype(np.float32))
