@@ -34,7 +34,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "talker"])
-    ap.add_argument("--also", default="prefill", help="comma-separated extra workloads ('' for none)")
+    ap.add_argument("--also", default="prefill,dense_prefill,decode_block",
+                    help="comma-separated extra workloads ('' for none): prefill, skew, talker, decode, "
+                         "dense_prefill, dense_decode (dense SwiGLU layers), decode_block (residual add + "
+                         "RMSNorm + the decode MoE layer, eager and replayed from a HIP graph)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -144,6 +147,66 @@ def bench_workload(name, steps, warmup, torch, moe):
     weight_bytes = res["hit_experts"] * 3 * cfg.I * cfg.H * 2 + cfg.I_shared * 3 * cfg.H * 2
     res["weight_hbm_frac"] = weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     return res
+
+
+def timed(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def bench_dense(name, steps, warmup, torch, moe):
+    """A dense SwiGLU layer (moe_dense_mlp) of hidden 2048, I = 6144."""
+    from sparse_moe_ffn_amd.inputs import DENSE_LAYERS, make_dense_inputs
+
+    L = DENSE_LAYERS[name]
+    t = make_dense_inputs(L["N"], L["H"], L["I"], device="cuda:0")
+    act = torch.empty((L["N"], L["I"]), dtype=t["x"].dtype, device="cuda:0")
+    out = torch.empty_like(t["x"])
+    ms = timed(lambda: moe.moe_dense_mlp(t["x"], t["w_gate_up"], t["w_down"], act=act, out=out), steps, warmup,
+               torch)
+    flops = 6.0 * L["N"] * L["H"] * L["I"]
+    wbytes = 3 * L["H"] * L["I"] * 2
+    return {"workload": f"{name}: dense SwiGLU layer N={L['N']} H={L['H']} I={L['I']} bf16",
+            "tokens_per_s": round(L["N"] / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "weight_hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def bench_decode_block(steps, warmup, torch, moe):
+    """Residual add + RMSNorm, then the decode MoE layer, issued eagerly and
+    replayed from one captured HIP graph."""
+    from sparse_moe_ffn_amd.inputs import CONFIGS, make_inputs, make_norm_inputs
+
+    cfg = CONFIGS["decode"]
+    t = make_inputs(cfg, "cuda:0")
+    n = make_norm_inputs(cfg.N, cfg.H, device="cuda:0")
+    res_out, normed, out = (torch.empty_like(n["x"]) for _ in range(3))
+    p = moe.problem_from(normed, t["w_gate_up"], t["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda:0")
+
+    def block():
+        moe.moe_add_rmsnorm(n["x"], n["residual"], n["weight"], 1e-6, residual_out=res_out, normed=normed)
+        moe.moe_forward(normed, t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                        out=out, workspace=ws)
+
+    eager = timed(block, steps, warmup, torch)
+    block()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        block()
+    replay = timed(graph.replay, steps, warmup, torch)
+    del graph
+    return {"workload": "decode_block: residual add + RMSNorm + the 64-token decode MoE layer",
+            "tokens_per_s": round(cfg.N / (replay * 1e-3), 1), "ms_per_step_graph": round(replay, 4),
+            "ms_per_step_eager": round(eager, 4)}
 
 
 GEMM_SOURCES = ("sparse_moe_ffn_amd/csrc/grouped_gemm.hip", "sparse_moe_ffn_amd/csrc/moe_common.h",
@@ -264,6 +327,14 @@ def main():
     also = {}
     for w in [s for s in a.also.split(",") if s and s != a.workload]:
         print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+        if w.startswith("dense_"):
+            also[w] = bench_dense(w, max(10, a.steps // 10), max(3, a.warmup // 4), torch, moe)
+            torch.cuda.empty_cache()
+            continue
+        if w == "decode_block":
+            also[w] = bench_decode_block(a.steps, a.warmup, torch, moe)
+            torch.cuda.empty_cache()
+            continue
         r = bench_workload(w, max(10, a.steps // 10), max(3, a.warmup // 4), torch, moe)
         also[w] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
                    "tflops": round(r["tflops"], 1), "mfma_frac": round(r["mfma_frac"], 4),

@@ -40,7 +40,8 @@
  * - An entry point validates only the moe_problem fields it uses (moe_route:
  *   tokens, hidden, experts, top_k, dtype, norm_topk_prob; moe_gate_up and
  *   moe_down add inter; moe_shared_expert: tokens, hidden, top_k, dtype and
- *   shared_inter; moe_combine: tokens, hidden, top_k, dtype).
+ *   shared_inter; moe_dense_mlp: tokens, hidden, top_k, dtype and inter;
+ *   moe_combine: tokens, hidden, top_k, dtype).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -188,6 +189,38 @@ int moe_shared_expert(const moe_problem* p, const void* x,
                       const void* shared_w_gate_up, const void* shared_w_down,
                       const float* shared_scale, void* shared_act,
                       void* shared_y, void* stream);
+
+/* Dense SwiGLU layer ("Qwen3.5 推理全流程" 2.5A Dense MLP; the nano-vLLM
+ * Qwen3 notes (lshu.cn/news/442807), Qwen3MLP / Qwen3MoeMLP of the layers in
+ * mlp_only_layers): the expert formula over every token, no router, no
+ * routing weight -- the E = k = 1 case of the block, on the same kernels as
+ * the shared expert:
+ *   act[n] = silu(x[n] Wg^T) * (x[n] Wu^T)        [N, I]  (caller's scratch)
+ *   out[n] = act[n] Wd^T                            [N, H]
+ *   w_gate_up [2I, H] (gate rows first), w_down [H, I], all dtype.
+ * Reads num_tokens, hidden, inter, top_k (any valid value) and dtype of p.
+ * out and act are fully overwritten. */
+int moe_dense_mlp(const moe_problem* p, const void* x, const void* w_gate_up,
+                  const void* w_down, void* act, void* out, void* stream);
+
+/* Residual add + RMSNorm in front of the block (the nano-vLLM Qwen3 notes
+ * (lshu.cn/news/442807), Qwen3DecoderLayer and question 4: the norm before
+ * the MLP adds the incoming activations to the residual stream, keeps the
+ * sum as the new residual and returns its normalisation, in one kernel;
+ * "Step 19: Real Model — Qwen3ForCausalLM", section "RMSNorm：去掉均值中心化"):
+ *   residual_out[n] = x[n] + residual_in[n]   (x[n] when residual_in is NULL:
+ *                     the first layer), summed in float32, rounded to dtype
+ *   normed[n]       = residual_out[n] / sqrt(mean_h residual_out[n,h]^2 + eps)
+ *                     * weight, float32, rounded once to dtype
+ *   x, residual_in, residual_out, normed [N, H] dtype;  weight [H] dtype.
+ * residual_out may be the same buffer as x or residual_in (each element is
+ * read before it is written, by the same thread); normed must not overlap
+ * residual_out.  hidden must be a multiple of 8 and at most 16384; eps > 0.
+ * One workgroup per token with a fixed reduction order, so a token's result
+ * does not depend on the batch. */
+int moe_add_rmsnorm(int64_t num_tokens, int64_t hidden, int32_t dtype,
+                    const void* x, const void* residual_in, void* residual_out,
+                    const void* weight, float eps, void* normed, void* stream);
 
 /* Deterministic combine (M03 逐步图 step 4 and 易错点: contributions of a
  * token's slots are added, never assigned):

@@ -73,6 +73,8 @@ def load_library() -> ctypes.CDLL:
             "moe_shared_expert": [PP, _P, _P, _P, _P, _P, _P, _P],
             "moe_combine": [PP, _P, _P, _P, _P],
             "moe_forward": [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+            "moe_dense_mlp": [PP, _P, _P, _P, _P, _P, _P],
+            "moe_add_rmsnorm": [_I64, _I64, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_float, _P, _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -291,6 +293,64 @@ def moe_combine(y, num_tokens: int, top_k: int, shared_y=None, out=None):
     with torch.cuda.device(dev):
         _check(load_library().moe_combine(ctypes.byref(p), _ptr(y), _ptr(shared_y), _ptr(out), _stream(dev)))
     return out
+
+
+def moe_dense_mlp(x, w_gate_up, w_down, act=None, out=None):
+    """Dense SwiGLU layer: out [N, H] = (silu(x Wg^T) * (x Wu^T)) Wd^T, with
+    w_gate_up [2I, H] (gate rows first) and w_down [H, I]; act [N, I] is the
+    intermediate (allocated when not given)."""
+    x = _gpu(x, "x")
+    dev = x.device
+    w_gate_up = _gpu(w_gate_up, "w_gate_up", x.dtype, dev)
+    w_down = _gpu(w_down, "w_down", x.dtype, dev)
+    N, H = x.shape
+    two_i, H2 = w_gate_up.shape
+    if H2 != H or two_i % 2 or tuple(w_down.shape) != (H, two_i // 2):
+        raise ValueError("shape mismatch between x, w_gate_up and w_down")
+    I = two_i // 2
+    p = problem(N, H, 1, 1, I, 0, x.dtype)
+    if act is None:
+        act = torch.empty((N, I), dtype=x.dtype, device=dev)
+    if out is None:
+        out = torch.empty_like(x)
+    for t, n, shape in ((act, "act", (N, I)), (out, "out", (N, H))):
+        _gpu(t, n, x.dtype, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{n} must have shape {shape}")
+    with torch.cuda.device(dev):
+        _check(load_library().moe_dense_mlp(ctypes.byref(p), _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(act),
+                                            _ptr(out), _stream(dev)))
+    return out
+
+
+def moe_add_rmsnorm(x, residual, weight, eps=1e-6, residual_out=None, normed=None):
+    """(normed, residual_out): residual_out = x + residual (x when residual is
+    None), normed = RMSNorm(residual_out) * weight.  residual_out may be
+    `residual` itself (in place)."""
+    x = _gpu(x, "x")
+    dev = x.device
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    N, H = x.shape
+    if residual is not None:
+        _gpu(residual, "residual", x.dtype, dev)
+        if residual.shape != x.shape:
+            raise ValueError("residual must have the shape of x")
+    weight = _gpu(weight, "weight", x.dtype, dev)
+    if weight.numel() != H:
+        raise ValueError("weight must have H elements")
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    if normed is None:
+        normed = torch.empty_like(x)
+    for t, n in ((residual_out, "residual_out"), (normed, "normed")):
+        _gpu(t, n, x.dtype, dev)
+        if t.shape != x.shape:
+            raise ValueError(f"{n} must have the shape of x")
+    with torch.cuda.device(dev):
+        _check(load_library().moe_add_rmsnorm(N, H, _DTYPES[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out),
+                                              _ptr(weight), float(eps), _ptr(normed), _stream(dev)))
+    return normed, residual_out
 
 
 _workspaces = {}

@@ -4,6 +4,10 @@
 //              act[r, i] = silu(x[tok] . Wg[e, i]) * (x[tok] . Wu[e, i])
 //   down:    y[p, h] = scale[p] * (act[r] . Wd[e, h])
 //
+// Dense mode (no grouping: every row of x through one weight set) serves the
+// shared expert and dense SwiGLU layers; its down product takes a per-row
+// scale, or none.
+//
 // "M03 · Sparse MoE：路由、按 expert 分组计算、shared expert", 题面速览 (expert
 // formula, one product per expert over its gathered tokens) and L1 细节
 // (Wg, Wu are [I, H], Wd is [H, I]); the gate rows precede the up rows in the
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
         float sc = 0.0f;
         if (r < rows_valid) {
           prow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
-          sc = g.scale[prow];
+          sc = g.scale ? g.scale[prow] : 1.0f;
         }
         ep_row[r] = prow;
         ep_scale[r] = sc;
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(kF32Threads) void grouped_gemm_f32_kernel(GemmProbl
       const float* wd = B + (int64_t)col * K;
       float acc = 0.f;
       for (int i = 0; i < K; ++i) acc = fmaf(ar[i], wd[i], acc);
-      C[prow * g.n_out + col] = g.scale[prow] * acc;
+      C[prow * g.n_out + col] = g.scale ? g.scale[prow] * acc : acc;
     }
   }
 }

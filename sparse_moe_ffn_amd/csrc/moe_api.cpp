@@ -87,9 +87,11 @@ int64_t choose_block_m(const moe_problem* p) {
   return 320;                       // one tile holds a typical prefill expert
 }
 
-// Row-tile height of the dense shared-expert products: tall tiles (fewer
-// bytes per flop) once there are enough rows to fill the GPU with them.
-int64_t shared_block_m(const moe_problem* p) {
+// Row-tile height of the dense products (shared expert, dense layers): tall
+// tiles (fewer bytes per flop) once there are enough rows to fill the GPU
+// with them.  Measured on the talker's shared expert (8192 rows, I_s = 2048):
+// 320-row tiles 199 us, 128-row tiles 218 us, 64-row tiles 308 us.
+int64_t dense_block_m(const moe_problem* p) {
   if (p->dtype == MOE_F32) return 16;
   const int64_t N = p->num_tokens;
   if (N >= 4096) return 320;
@@ -155,6 +157,32 @@ int check_ptrs_bf16(const moe_problem* p, std::initializer_list<const void*> ptr
     if (q && p->dtype == MOE_BF16 && !aligned16(q))
       return fail(MOE_EUNSUPPORTED, "bf16 tensors must be 16-byte aligned");
   return MOE_OK;
+}
+
+// Dense SwiGLU over all rows of x: act = silu(x Wg^T) * (x Wu^T), then
+// c = scale[n] * (act Wd^T) (scale NULL: 1).
+int dense_swiglu(const moe_problem* p, int64_t inter, const void* x, const void* w_gate_up,
+                 const void* w_down, const float* scale, void* act, void* c, hipStream_t stream,
+                 const char* what_gate_up, const char* what_down) {
+  const int64_t N = p->num_tokens;
+  const int64_t bm = dense_block_m(p);
+  moe::GemmProblem g = gemm_common(p);
+  g.dense_rows = (int32_t)N;
+  g.block_m = (int32_t)bm;
+  g.max_tiles = (int32_t)((N + bm - 1) / bm);
+  g.a = x;
+  g.b = w_gate_up;
+  g.c = act;
+  g.K = (int32_t)p->hidden;
+  g.n_out = (int32_t)inter;
+  if (int rc = hip_status(moe::launch_gate_up(g, stream), what_gate_up)) return rc;
+  g.a = act;
+  g.b = w_down;
+  g.c = c;
+  g.scale = scale;
+  g.K = (int32_t)inter;
+  g.n_out = (int32_t)p->hidden;
+  return hip_status(moe::launch_down(g, stream), what_down);
 }
 
 }  // namespace
@@ -297,25 +325,37 @@ int moe_shared_expert(const moe_problem* p, const void* x, const void* shared_w_
   if (!x || !shared_w_gate_up || !shared_w_down || !shared_scale || !shared_act || !shared_y)
     return fail(MOE_EINVAL, "NULL tensor");
   if (int rc = check_ptrs_bf16(p, {x, shared_w_gate_up, shared_w_down, shared_act, shared_y})) return rc;
-  const int64_t N = p->num_tokens;
-  const int64_t bm = shared_block_m(p);
-  moe::GemmProblem g = gemm_common(p);
-  g.dense_rows = (int32_t)N;
-  g.block_m = (int32_t)bm;
-  g.max_tiles = (int32_t)((N + bm - 1) / bm);
-  g.a = x;
-  g.b = shared_w_gate_up;
-  g.c = shared_act;
-  g.K = (int32_t)p->hidden;
-  g.n_out = (int32_t)p->shared_inter;
-  if (int rc = hip_status(moe::launch_gate_up(g, (hipStream_t)stream), "shared gate_up")) return rc;
-  g.a = shared_act;
-  g.b = shared_w_down;
-  g.c = shared_y;
-  g.scale = shared_scale;
-  g.K = (int32_t)p->shared_inter;
-  g.n_out = (int32_t)p->hidden;
-  return hip_status(moe::launch_down(g, (hipStream_t)stream), "shared down") ?: ok();
+  return dense_swiglu(p, p->shared_inter, x, shared_w_gate_up, shared_w_down, shared_scale, shared_act,
+                      shared_y, (hipStream_t)stream, "shared gate_up", "shared down") ?: ok();
+}
+
+int moe_dense_mlp(const moe_problem* p, const void* x, const void* w_gate_up, const void* w_down, void* act,
+                  void* out, void* stream) {
+  if (int rc = check_problem(p, kUsesInter)) return rc;
+  if (p->num_tokens == 0) return ok();
+  if (!x || !w_gate_up || !w_down || !act || !out) return fail(MOE_EINVAL, "NULL tensor");
+  if (int rc = check_ptrs_bf16(p, {x, w_gate_up, w_down, act, out})) return rc;
+  return dense_swiglu(p, p->inter, x, w_gate_up, w_down, nullptr, act, out, (hipStream_t)stream,
+                      "dense gate_up", "dense down") ?: ok();
+}
+
+int moe_add_rmsnorm(int64_t num_tokens, int64_t hidden, int32_t dtype, const void* x, const void* residual_in,
+                    void* residual_out, const void* weight, float eps, void* normed, void* stream) {
+  if (num_tokens < 0 || hidden < 1) return fail(MOE_EINVAL, "need num_tokens >= 0 and hidden >= 1");
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "unknown dtype");
+  if (hidden % 8 || hidden > moe::add_rmsnorm_max_hidden())
+    return fail(MOE_EUNSUPPORTED, "hidden must be a multiple of 8 and at most %lld",
+                (long long)moe::add_rmsnorm_max_hidden());
+  if (num_tokens >= ((int64_t)1 << 31) || num_tokens * hidden >= ((int64_t)1 << 40))
+    return fail(MOE_EUNSUPPORTED, "sizes too large");
+  if (!(eps > 0.0f) || !(eps < 1e30f)) return fail(MOE_EINVAL, "eps must be positive and finite");
+  if (num_tokens == 0) return ok();
+  if (!x || !residual_out || !weight || !normed) return fail(MOE_EINVAL, "NULL tensor");
+  if (normed == residual_out) return fail(MOE_EINVAL, "normed and residual_out must be different buffers");
+  for (const void* q : {x, residual_in, (const void*)residual_out, weight, (const void*)normed})
+    if (q && !aligned16(q)) return fail(MOE_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  return hip_status(moe::launch_add_rmsnorm(x, residual_in, residual_out, weight, normed, num_tokens, hidden, eps,
+                                            dtype, (hipStream_t)stream), "add_rmsnorm") ?: ok();
 }
 
 int moe_combine(const moe_problem* p, const void* y, const void* shared_y, void* out, void* stream) {

@@ -35,7 +35,7 @@ struct GemmProblem {
   const int32_t* tile_expert;
   const int32_t* tile_rows;
   const int32_t* num_tiles;
-  const float* scale;          // down only: per-pair (grouped) or per-row (dense) factor
+  const float* scale;          // down only: per-pair (grouped) or per-row (dense) factor; nullptr: 1
   void* c;                     // gate/up: act [rows, Nout];  down: y [pairs or rows, Nout]
   int64_t expert_stride;       // elements
   int32_t K;                   // reduction length
@@ -50,6 +50,11 @@ struct GemmProblem {
 
 hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s);
 hipError_t launch_down(const GemmProblem& g, hipStream_t s);
+
+// residual_out = x (+ residual_in); normed = RMSNorm(residual_out) * weight.
+int64_t add_rmsnorm_max_hidden();
+hipError_t launch_add_rmsnorm(const void* x, const void* residual_in, void* residual_out, const void* weight,
+                              void* normed, int64_t N, int64_t H, float eps, int32_t dtype, hipStream_t s);
 
 // out[n] = sum_j y[n*k + j] (+ shared_y[n]), float32 sum in slot order.
 hipError_t launch_combine(const void* y, const void* shared_y, void* out, int64_t N, int64_t H,

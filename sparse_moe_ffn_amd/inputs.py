@@ -40,7 +40,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 import torch
 
-__all__ = ["MoEConfig", "CONFIGS", "make_inputs", "skew_biases", "zipf_targets"]
+__all__ = ["MoEConfig", "CONFIGS", "DENSE_LAYERS", "make_inputs", "make_dense_inputs", "make_norm_inputs",
+           "skew_biases", "zipf_targets"]
 
 
 @dataclass(frozen=True)
@@ -189,6 +190,39 @@ def make_inputs(cfg: MoEConfig, device="cpu") -> dict:
         out["router_w"][:, 0] = b.to(device=device, dtype=dt)
         out["skew_perm"] = perm
     return out
+
+
+# Dense SwiGLU layers of hidden 2048 with I = 6144 = 8 * 768: the same work
+# per token as the 8 routed experts of the MoE layer above.
+DENSE_LAYERS = {
+    "dense_decode": dict(N=64, H=2048, I=6144),
+    "dense_prefill": dict(N=4096, H=2048, I=6144),
+}
+
+
+def make_dense_inputs(N, H, I, dtype="bf16", seed=0, std=0.02, device="cpu") -> dict:
+    """x [N, H] (std 1), w_gate_up [2I, H] and w_down [H, I] (std `std`), drawn
+    in that order, each randn * std rounded once to the dtype."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    return {"x": _randn((N, H), g, device, 1.0, dt), "w_gate_up": _randn((2 * I, H), g, device, std, dt),
+            "w_down": _randn((H, I), g, device, std, dt)}
+
+
+def make_norm_inputs(N, H, dtype="bf16", seed=0, device="cpu") -> dict:
+    """Inputs of the residual add + RMSNorm: x [N, H] (the sub-layer output,
+    std 1), residual [N, H] (std 1) and the norm weight [H] = 1 + 0.1 * randn,
+    drawn in that order and rounded once to the dtype."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = _randn((N, H), g, device, 1.0, dt)
+    residual = _randn((N, H), g, device, 1.0, dt)
+    w = torch.randn((H,), generator=g, device=device, dtype=torch.float32).mul_(0.1).add_(1.0).to(dt)
+    return {"x": x, "residual": residual, "weight": w}
 
 
 def random_case(N, H, E, top_k, I, I_shared=0, dtype="bf16", norm_topk_prob=True,

@@ -98,3 +98,26 @@ def test_forward_rejects_before_any_hip_call():
     # empty batch: valid, nothing to do
     p0 = moe.problem(0, 64, 4, 2, 64)
     assert lib.moe_forward(ctypes.byref(p0), None, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_dense_mlp_and_add_rmsnorm_reject_before_any_hip_call():
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    p = moe.problem(16, 64, 1, 1, 96)                        # bf16 inter must be a multiple of 64
+    assert lib.moe_dense_mlp(ctypes.byref(p), fake, fake, fake, fake, fake, None) == B.MOE_EUNSUPPORTED
+    p = moe.problem(16, 64, 1, 1, 128)
+    assert lib.moe_dense_mlp(ctypes.byref(p), fake, None, fake, fake, fake, None) == B.MOE_EINVAL
+    assert lib.moe_dense_mlp(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 8), fake, fake, fake, fake,
+                             None) == B.MOE_EUNSUPPORTED
+    p0 = moe.problem(0, 64, 1, 1, 128)
+    assert lib.moe_dense_mlp(ctypes.byref(p0), None, None, None, None, None, None) == 0
+    f = lib.moe_add_rmsnorm
+    other = ctypes.c_void_p(1 << 21)
+    assert f(4, 60, B.MOE_BF16, fake, None, fake, fake, 1e-6, other, None) == B.MOE_EUNSUPPORTED   # H % 8
+    assert f(4, 32768, B.MOE_BF16, fake, None, fake, fake, 1e-6, other, None) == B.MOE_EUNSUPPORTED
+    assert f(4, 64, B.MOE_BF16, fake, None, fake, fake, 0.0, other, None) == B.MOE_EINVAL          # eps > 0
+    assert f(4, 64, B.MOE_BF16, fake, None, fake, fake, float("nan"), other, None) == B.MOE_EINVAL
+    assert f(4, 64, B.MOE_BF16, fake, None, fake, fake, 1e-6, fake, None) == B.MOE_EINVAL          # normed aliases
+    assert f(4, 64, B.MOE_BF16, None, None, fake, fake, 1e-6, other, None) == B.MOE_EINVAL
+    assert f(4, 64, 7, fake, None, fake, fake, 1e-6, other, None) == B.MOE_EUNSUPPORTED
+    assert f(0, 64, B.MOE_BF16, None, None, None, None, 1e-6, None, None) == 0
