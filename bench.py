@@ -3,7 +3,10 @@
 
 One step = one full pass of the block (router, align, gate/up, down,
 [shared expert], combine) over one batch of seeded synthetic tokens already
-resident in HBM, through the C ABI (``moe_forward``).
+resident in HBM, through the C ABI (``moe_forward``).  Expert weights are
+packed once into the library's blocked layout before timing (a weight-load
+step, ``moe_pack_weights``); the same step with row-major weights is timed
+too and reported as ``ms_per_step_row_major``.
 
 Prints ONE JSON line.  ``value`` is tokens/s of the main workload (default:
 the 64-token decode layer, H=2048, E=128, top-8, I=768, bf16).  ``roofline``
@@ -73,20 +76,26 @@ def bench_workload(name, steps, warmup, torch, moe):
     cfg = CONFIGS[name]
     dev = torch.device("cuda:0")
     t = make_inputs(cfg, dev)
-    args = (t["x"], t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
-            t["shared_w_gate_up"], t["shared_w_down"], t["shared_gate"])
+    blk = moe.MOE_LAYOUT_BLOCKED
+    tw = {k: (moe.moe_pack_weights(t[k]) if t[k] is not None else None)
+          for k in ("w_gate_up", "w_down", "shared_w_gate_up", "shared_w_down")}
+    args = (t["x"], t["router_w"], tw["w_gate_up"], tw["w_down"], cfg.top_k, cfg.norm_topk_prob,
+            tw["shared_w_gate_up"], tw["shared_w_down"], t["shared_gate"])
+    args_rm = (t["x"], t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
+               t["shared_w_gate_up"], t["shared_w_down"], t["shared_gate"])
     p = moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], cfg.top_k, cfg.norm_topk_prob,
-                         t["shared_w_gate_up"])
+                         t["shared_w_gate_up"], blk)
     ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["x"])
     for _ in range(warmup):
-        moe.moe_forward(*args, out=out, workspace=ws)
+        moe.moe_forward(*args, out=out, workspace=ws, weight_layout=blk)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        moe.moe_forward(*args, out=out, workspace=ws)
+        moe.moe_forward(*args, out=out, workspace=ws, weight_layout=blk)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    ms_row_major = timed(lambda: moe.moe_forward(*args_rm, out=out, workspace=ws), steps, warmup, torch)
 
     # Same stages issued one by one, HIP events between them, on the stream
     # the kernels run on (torch's current stream).
@@ -113,13 +122,14 @@ def bench_workload(name, steps, warmup, torch, moe):
         e[1].record()
         g2 = moe.moe_align(ids, cfg.E, bm, align_scratch)
         e[2].record()
-        moe.moe_gate_up(t["x"], t["w_gate_up"], g2, cfg.top_k, act)
+        moe.moe_gate_up(t["x"], tw["w_gate_up"], g2, cfg.top_k, act, weight_layout=blk)
         e[3].record()
-        moe.moe_down(act, t["w_down"], wts, g2, cfg.N, cfg.top_k, y)
+        moe.moe_down(act, tw["w_down"], wts, g2, cfg.N, cfg.top_k, y, weight_layout=blk)
         e[4].record()
         i = 5
         if cfg.I_shared:
-            moe.moe_shared_expert(t["x"], t["shared_w_gate_up"], t["shared_w_down"], sscale, sact, sy)
+            moe.moe_shared_expert(t["x"], tw["shared_w_gate_up"], tw["shared_w_down"], sscale, sact, sy,
+                                  weight_layout=blk)
             e[i].record()
             i += 1
         moe.moe_combine(y, cfg.N, cfg.top_k, sy, out)
@@ -139,6 +149,7 @@ def bench_workload(name, steps, warmup, torch, moe):
     ms = elapsed / steps * 1e3
     res = {
         "cfg": cfg, "inputs": t, "ms_per_step": ms, "tokens_per_s": cfg.N / (ms * 1e-3),
+        "ms_per_step_row_major": ms_row_major,
         "tflops": cfg.flops() / (ms * 1e-3) / 1e12, "stage_ms": stage_ms, "work": work,
         "hit_experts": expert_hits(counts), "counts_min_max": [int(counts.min()), int(counts.max())],
         "block_m": bm,
@@ -168,8 +179,9 @@ def bench_dense(name, steps, warmup, torch, moe):
     t = make_dense_inputs(L["N"], L["H"], L["I"], device="cuda:0")
     act = torch.empty((L["N"], L["I"]), dtype=t["x"].dtype, device="cuda:0")
     out = torch.empty_like(t["x"])
-    ms = timed(lambda: moe.moe_dense_mlp(t["x"], t["w_gate_up"], t["w_down"], act=act, out=out), steps, warmup,
-               torch)
+    wgu, wd = moe.moe_pack_weights(t["w_gate_up"]), moe.moe_pack_weights(t["w_down"])
+    ms = timed(lambda: moe.moe_dense_mlp(t["x"], wgu, wd, act=act, out=out, weight_layout=moe.MOE_LAYOUT_BLOCKED),
+               steps, warmup, torch)
     flops = 6.0 * L["N"] * L["H"] * L["I"]
     wbytes = 3 * L["H"] * L["I"] * 2
     return {"workload": f"{name}: dense SwiGLU layer N={L['N']} H={L['H']} I={L['I']} bf16",
@@ -190,11 +202,12 @@ def bench_decode_block(steps, warmup, torch, moe):
     res_out, normed, out = (torch.empty_like(n["x"]) for _ in range(3))
     p = moe.problem_from(normed, t["w_gate_up"], t["router_w"], cfg.top_k, cfg.norm_topk_prob)
     ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device="cuda:0")
+    wgu, wd = moe.moe_pack_weights(t["w_gate_up"]), moe.moe_pack_weights(t["w_down"])
 
     def block():
         moe.moe_add_rmsnorm(n["x"], n["residual"], n["weight"], 1e-6, residual_out=res_out, normed=normed)
-        moe.moe_forward(normed, t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
-                        out=out, workspace=ws)
+        moe.moe_forward(normed, t["router_w"], wgu, wd, cfg.top_k, cfg.norm_topk_prob,
+                        out=out, workspace=ws, weight_layout=moe.MOE_LAYOUT_BLOCKED)
 
     eager = timed(block, steps, warmup, torch)
     block()
@@ -258,7 +271,7 @@ def roofline_for(res):
     w = res["work"][kern]
     gbs = w["bytes"] / dur_s / 1e9
     tfs = w["flops"] / dur_s / 1e12
-    common = {"kernel": f"grouped_gemm_bf16 gate_up (SwiGLU epilogue), block_m {res['block_m']}",
+    common = {"kernel": f"grouped_gemm_bf16 gate_up (SwiGLU epilogue), block_m {res['block_m']}, blocked weights",
               "traffic": measured_traffic(cfg.name), "avg_launch_ms": round(res["stage_ms"][kern], 4),
               "algorithmic_bytes_per_launch": w["bytes"], "algorithmic_flops_per_launch": w["flops"],
               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
@@ -285,17 +298,24 @@ def cpu_baseline(res, budget_s, torch):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing: numpy's BLAS default
         cores = os.cpu_count()
+    # Whole passes over the batch (routing of every token, then the expert
+    # math token by token) until the budget is spent; a pass that does not
+    # fit the budget stops at the token where the budget ran out.
     t0 = time.perf_counter()
-    routing = O.route(h["x"], h["router_w"], cfg.top_k, cfg.norm_topk_prob)
-    done = 0
-    while done < cfg.N and (time.perf_counter() - t0) < budget_s:
-        O.moe_forward(h["x"], h["router_w"], h["w_gate_up"], h["w_down"], cfg.top_k, cfg.norm_topk_prob,
-                      shared=sh, rows=[done], routing=routing)
-        done += 1
+    done = passes = 0
+    while (time.perf_counter() - t0) < budget_s:
+        routing = O.route(h["x"], h["router_w"], cfg.top_k, cfg.norm_topk_prob)
+        n = 0
+        while n < cfg.N and (time.perf_counter() - t0) < budget_s:
+            O.moe_forward(h["x"], h["router_w"], h["w_gate_up"], h["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                          shared=sh, rows=[n], routing=routing)
+            n += 1
+        done += n
+        passes += n == cfg.N
     el = time.perf_counter() - t0
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {done} of {cfg.N} tokens of the {cfg.name} layer (routing of all {cfg.N}), "
-                      f"{el:.1f} s, numpy float64 expert math"}
+            "sample": f"{done} tokens of the {cfg.name} layer ({passes} whole passes over its {cfg.N} tokens, "
+                      f"each routing the whole batch), {el:.1f} s, numpy float64 expert math"}
 
 
 def copy_calibration(torch):
@@ -337,6 +357,7 @@ def main():
             continue
         r = bench_workload(w, max(10, a.steps // 10), max(3, a.warmup // 4), torch, moe)
         also[w] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                   "ms_per_step_row_major": round(r["ms_per_step_row_major"], 4),
                    "tflops": round(r["tflops"], 1), "mfma_frac": round(r["mfma_frac"], 4),
                    "weight_hbm_frac": round(r["weight_hbm_frac"], 4),
                    "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
@@ -356,7 +377,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: Qwen3-30B-A3B-shaped MoE layer", "tokens": cfg.N, "hidden": cfg.H,
                    "experts": cfg.E, "top_k": cfg.top_k, "inter": cfg.I, "shared_inter": cfg.I_shared,
-                   "norm_topk_prob": cfg.norm_topk_prob, "seed": cfg.seed},
+                   "norm_topk_prob": cfg.norm_topk_prob, "seed": cfg.seed, "weight_layout": "blocked"},
+        "ms_per_step_row_major": round(main_res["ms_per_step_row_major"], 5),
         "tflops": round(main_res["tflops"], 2), "mfma_frac": round(main_res["mfma_frac"], 4),
         "weight_hbm_frac": round(main_res["weight_hbm_frac"], 4),
         "stage_ms": {k: round(v, 4) for k, v in main_res["stage_ms"].items()},

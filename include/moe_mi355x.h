@@ -37,6 +37,9 @@
  *   moe_last_error() describes the problem.  num_tokens == 0 is valid and
  *   enqueues nothing.
  * - Limits: 1 <= top_k <= num_experts <= 512, top_k <= 32.
+ * - Expert weights are row-major unless p->weight_layout is
+ *   MOE_LAYOUT_BLOCKED (see moe_pack_weights); shapes below are the
+ *   row-major ones.
  * - An entry point validates only the moe_problem fields it uses (moe_route:
  *   tokens, hidden, experts, top_k, dtype, norm_topk_prob; moe_gate_up and
  *   moe_down add inter; moe_shared_expert: tokens, hidden, top_k, dtype and
@@ -63,7 +66,14 @@ enum {
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
-/* Shape and options of one MoE layer call. */
+/* Storage of the expert weights (w_gate_up, w_down, and the shared-expert
+ * and dense-layer weights; the router weight and the shared gate are always
+ * row-major).  MOE_LAYOUT_ROW_MAJOR is the shapes as written (M03 L1 细节);
+ * MOE_LAYOUT_BLOCKED is what moe_pack_weights produces (bf16 only). */
+enum { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_BLOCKED = 1 };
+
+/* Shape and options of one MoE layer call.  A zero-initialised struct with
+ * the sizes filled in means row-major weights. */
 typedef struct moe_problem {
   int64_t num_tokens;      /* N  */
   int64_t hidden;          /* H  */
@@ -73,6 +83,8 @@ typedef struct moe_problem {
   int64_t shared_inter;    /* I_s: shared-expert intermediate size, 0 = none */
   int32_t dtype;           /* MOE_F32 or MOE_BF16 */
   int32_t norm_topk_prob;  /* 1: renormalise the k kept weights to sum 1 */
+  int32_t weight_layout;   /* MOE_LAYOUT_ROW_MAJOR or MOE_LAYOUT_BLOCKED */
+  int32_t reserved;        /* must be 0 */
 } moe_problem;
 
 /* Byte offsets of the regions moe_forward carves out of its workspace, and
@@ -92,6 +104,24 @@ typedef struct moe_workspace_layout {
  * Pure host arithmetic; never touches the GPU. */
 int moe_workspace_size(const moe_problem* p, size_t* bytes);
 int moe_get_workspace_layout(const moe_problem* p, moe_workspace_layout* layout);
+
+/* Expert weights in the blocked layout.  The pages fix only the weight
+ * shapes (M03 L1 细节: Wg, Wu [I, H], Wd [H, I]); the layout is this
+ * library's.  Each group of 8 rows is stored as consecutive 1 KB blocks of
+ * 8 rows x 64 columns, so one K stage of a grouped product reads whole
+ * blocks instead of 128 bytes from each of 8 rows 2*cols bytes apart; the
+ * products then run a few per cent faster and give bit for bit the same
+ * results as with row-major weights.  Meant as a one-time step when the
+ * weights are loaded.
+ *   src [batch, rows, cols] bf16 row-major; dst the same number of bf16
+ *   elements, element (b, r, c) at
+ *     b*rows*cols + ((r/8)*(cols/64) + c/64)*512 + (r%8)*64 + c%64.
+ *   w_gate_up: batch E, rows 2I, cols H;  w_down: batch E, rows H, cols I;
+ *   shared expert and dense layers: batch 1.
+ * dtype must be MOE_BF16; rows % 8 == 0 and cols % 64 == 0; src and dst
+ * 16-byte aligned and not overlapping.  Asynchronous on stream. */
+int moe_pack_weights(int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
+                     const void* src, void* dst, void* stream);
 
 /* Capacity of the padded grouping for num_pairs pairs over num_experts
  * experts with tile height block_m: max_rows = max_tiles * block_m, where

@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 
 MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
+MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_BLOCKED = 0, 1
 
 _DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 
@@ -35,7 +36,8 @@ class MoEProblem(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("num_experts", ctypes.c_int64), ("top_k", ctypes.c_int64),
                 ("inter", ctypes.c_int64), ("shared_inter", ctypes.c_int64),
-                ("dtype", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class MoEWorkspaceLayout(ctypes.Structure):
@@ -75,6 +77,7 @@ def load_library() -> ctypes.CDLL:
             "moe_forward": [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
             "moe_dense_mlp": [PP, _P, _P, _P, _P, _P, _P],
             "moe_add_rmsnorm": [_I64, _I64, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_float, _P, _P],
+            "moe_pack_weights": [_I64, _I64, _I64, ctypes.c_int32, _P, _P, _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -114,20 +117,39 @@ def _gpu(t: torch.Tensor, name: str, dtype=None, device=None) -> torch.Tensor:
 
 
 def problem(num_tokens, hidden, num_experts, top_k, inter, shared_inter=0, dtype=torch.bfloat16,
-            norm_topk_prob=True) -> MoEProblem:
+            norm_topk_prob=True, weight_layout=MOE_LAYOUT_ROW_MAJOR) -> MoEProblem:
     if dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {dtype}")
     return MoEProblem(int(num_tokens), int(hidden), int(num_experts), int(top_k), int(inter),
-                      int(shared_inter), _DTYPES[dtype], int(bool(norm_topk_prob)))
+                      int(shared_inter), _DTYPES[dtype], int(bool(norm_topk_prob)), int(weight_layout), 0)
 
 
-def problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up=None) -> MoEProblem:
+def problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up=None,
+                 weight_layout=MOE_LAYOUT_ROW_MAJOR) -> MoEProblem:
     N, H = x.shape
     E, two_i, H2 = w_gate_up.shape
     if H2 != H or two_i % 2 or router_w.shape != (E, H):
         raise ValueError("shape mismatch between x, router_w and w_gate_up")
     Is = 0 if shared_w_gate_up is None else shared_w_gate_up.shape[0] // 2
-    return problem(N, H, E, top_k, two_i // 2, Is, x.dtype, norm_topk_prob)
+    return problem(N, H, E, top_k, two_i // 2, Is, x.dtype, norm_topk_prob, weight_layout)
+
+
+def moe_pack_weights(w, out=None):
+    """`w` ([rows, cols] or [batch, rows, cols], bf16, row-major) in the
+    blocked layout of moe_pack_weights: a tensor of the same shape whose
+    storage holds the blocks (index it only through the library)."""
+    w = _gpu(w, "w", torch.bfloat16)
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [rows, cols] or [batch, rows, cols]")
+    batch, rows, cols = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    if out is None:
+        out = torch.empty_like(w)
+    _gpu(out, "out", torch.bfloat16, w.device)
+    if out.shape != w.shape:
+        raise ValueError("out must have the shape of w")
+    with torch.cuda.device(w.device):
+        _check(load_library().moe_pack_weights(batch, rows, cols, MOE_BF16, _ptr(w), _ptr(out), _stream(w.device)))
+    return out
 
 
 def moe_workspace_size(p: MoEProblem) -> int:
@@ -223,14 +245,14 @@ def moe_align(topk_ids, num_experts: int, block_m: int, scratch=None) -> Groupin
     return g
 
 
-def moe_gate_up(x, w_gate_up, grouping: Grouping, top_k: int, act=None):
+def moe_gate_up(x, w_gate_up, grouping: Grouping, top_k: int, act=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """act [max_rows, I] in x.dtype (rows of sentinel pairs are not written)."""
     x = _gpu(x, "x")
     dev = x.device
     w_gate_up = _gpu(w_gate_up, "w_gate_up", x.dtype, dev)
     N, H = x.shape
     E, two_i, _ = w_gate_up.shape
-    p = problem(N, H, E, top_k, two_i // 2, 0, x.dtype)
+    p = problem(N, H, E, top_k, two_i // 2, 0, x.dtype, weight_layout=weight_layout)
     if act is None:
         act = torch.empty((grouping.max_rows, two_i // 2), dtype=x.dtype, device=dev)
     with torch.cuda.device(dev):
@@ -241,14 +263,15 @@ def moe_gate_up(x, w_gate_up, grouping: Grouping, top_k: int, act=None):
     return act
 
 
-def moe_down(act, w_down, topk_w, grouping: Grouping, num_tokens: int, top_k: int, y=None):
+def moe_down(act, w_down, topk_w, grouping: Grouping, num_tokens: int, top_k: int, y=None,
+             weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """y [N*k, H] in act.dtype: y[p] = topk_w[p] * (act[row of p] . w_down[e]^T)."""
     act = _gpu(act, "act")
     dev = act.device
     w_down = _gpu(w_down, "w_down", act.dtype, dev)
     topk_w = _gpu(topk_w, "topk_w", torch.float32, dev)
     E, H, I = w_down.shape
-    p = problem(num_tokens, H, E, top_k, I, 0, act.dtype)
+    p = problem(num_tokens, H, E, top_k, I, 0, act.dtype, weight_layout=weight_layout)
     if y is None:
         y = torch.empty((num_tokens * top_k, H), dtype=act.dtype, device=dev)
     with torch.cuda.device(dev):
@@ -259,7 +282,8 @@ def moe_down(act, w_down, topk_w, grouping: Grouping, num_tokens: int, top_k: in
     return y
 
 
-def moe_shared_expert(x, shared_w_gate_up, shared_w_down, shared_scale, shared_act=None, shared_y=None):
+def moe_shared_expert(x, shared_w_gate_up, shared_w_down, shared_scale, shared_act=None, shared_y=None,
+                      weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """(shared_act [N, I_s], shared_y [N, H] = shared_scale[:, None] * SwiGLU_s(x))."""
     x = _gpu(x, "x")
     dev = x.device
@@ -268,7 +292,7 @@ def moe_shared_expert(x, shared_w_gate_up, shared_w_down, shared_scale, shared_a
     shared_scale = _gpu(shared_scale, "shared_scale", torch.float32, dev)
     N, H = x.shape
     Is = shared_w_gate_up.shape[0] // 2
-    p = problem(N, H, 1, 1, 1, Is, x.dtype)
+    p = problem(N, H, 1, 1, 1, Is, x.dtype, weight_layout=weight_layout)
     if shared_act is None:
         shared_act = torch.empty((N, Is), dtype=x.dtype, device=dev)
     if shared_y is None:
@@ -295,7 +319,7 @@ def moe_combine(y, num_tokens: int, top_k: int, shared_y=None, out=None):
     return out
 
 
-def moe_dense_mlp(x, w_gate_up, w_down, act=None, out=None):
+def moe_dense_mlp(x, w_gate_up, w_down, act=None, out=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """Dense SwiGLU layer: out [N, H] = (silu(x Wg^T) * (x Wu^T)) Wd^T, with
     w_gate_up [2I, H] (gate rows first) and w_down [H, I]; act [N, I] is the
     intermediate (allocated when not given)."""
@@ -308,7 +332,7 @@ def moe_dense_mlp(x, w_gate_up, w_down, act=None, out=None):
     if H2 != H or two_i % 2 or tuple(w_down.shape) != (H, two_i // 2):
         raise ValueError("shape mismatch between x, w_gate_up and w_down")
     I = two_i // 2
-    p = problem(N, H, 1, 1, I, 0, x.dtype)
+    p = problem(N, H, 1, 1, I, 0, x.dtype, weight_layout=weight_layout)
     if act is None:
         act = torch.empty((N, I), dtype=x.dtype, device=dev)
     if out is None:
@@ -368,8 +392,10 @@ def workspace_for(p: MoEProblem, device) -> torch.Tensor:
 
 
 def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob=True, shared_w_gate_up=None,
-                shared_w_down=None, shared_gate=None, out=None, workspace=None):
-    """The whole block: out [N, H] in x.dtype."""
+                shared_w_down=None, shared_gate=None, out=None, workspace=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
+    """The whole block: out [N, H] in x.dtype.  With weight_layout
+    MOE_LAYOUT_BLOCKED the expert (and shared-expert) weights are the
+    outputs of moe_pack_weights."""
     x = _gpu(x, "x")
     dev = x.device
     for t, n in ((router_w, "router_w"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
@@ -378,7 +404,7 @@ def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob=True, shar
                  (shared_gate, "shared_gate")):
         if t is not None:
             _gpu(t, n, x.dtype, dev)
-    p = problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up)
+    p = problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up, weight_layout)
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:

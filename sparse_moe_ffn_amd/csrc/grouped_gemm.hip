@@ -85,9 +85,10 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 constexpr bool kRotateK = true;
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
   static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(!BLK || BK == 64, "blocked weights come in 64-column blocks, one per stage");
   constexpr int kCpr = BK / 8;                      // 16-byte chunks per staged row
   constexpr int kRowsPerDma = kDmaBytes / (BK * 2); // rows one wave-wide DMA fills
   constexpr int NW = WAVES_M * WAVES_N;
@@ -191,7 +192,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
                         : min((int64_t)g.n_out + nt * half + (j - half), b_rows - 1);
     else
       wrow = min((int64_t)nt * BN + j, b_rows - 1);
-    src_b[q] = B + wrow * K + chunk * 8;
+    // Row-major: row wrow starts at wrow * K.  Blocked: the 8-row group of
+    // wrow starts at (wrow / 8) * 8K, its 64-column blocks follow one
+    // another (512 elements each), and row wrow % 8 sits 64 * (wrow % 8)
+    // into each block; issue_b scales the K offset by 8 to match.
+    src_b[q] = (BLK ? B + (wrow >> 3) * ((int64_t)K * 8) + (wrow & 7) * 64 : B + wrow * K) + chunk * 8;
   }
 
   const int nk = K / BK;
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   };
   auto issue_b = [&](int kt) {
     const uint32_t base = lds_addr(ring_b + (kt % SB) * kBStage);
-    const int ko = kpos(kt);
+    const int ko = BLK ? kpos(kt) * 8 : kpos(kt);
 #pragma unroll
     for (int q = 0; q < B_PER_WAVE; ++q)
       if (q < kBFull || wave < kBRem) dma16(src_b[q] + ko, base + (wave + NW * q) * kDmaBytes);
@@ -457,6 +462,31 @@ __global__ __launch_bounds__(kF32Threads) void grouped_gemm_f32_kernel(GemmProbl
   }
 }
 
+// ---------------------------------------------------------------- weight packing
+// dst (blocked) from src (row-major [batch, rows, cols]): each thread moves one
+// 16-byte piece (8 elements of one row inside one 64-column block).
+__global__ __launch_bounds__(256) void pack_weights_bf16_kernel(const uint16_t* __restrict__ src,
+                                                                uint16_t* __restrict__ dst, int64_t pieces,
+                                                                int64_t rows, int64_t cols) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const int64_t per_row = cols / 8;
+  const int64_t r_all = i / per_row;                 // batch * rows + row
+  const int64_t c = (i % per_row) * 8;               // first column of the piece
+  const int64_t b = r_all / rows, r = r_all % rows;
+  const int64_t d = b * rows * cols + ((r >> 3) * (cols / 64) + (c >> 6)) * 512 + (r & 7) * 64 + (c & 63);
+  *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(src + r_all * cols + c);
+}
+
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols,
+                               hipStream_t s) {
+  const int64_t pieces = batch * rows * cols / 8;
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_weights_bf16_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s,
+                     (const uint16_t*)src, (uint16_t*)dst, pieces, rows, cols);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE>
@@ -465,8 +495,12 @@ static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
   const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE>),
-                     dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+  if (g.weights_blocked)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true>),
+                       dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false>),
+                       dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
   return hipGetLastError();
 }
 

@@ -46,6 +46,11 @@ int check_problem(const moe_problem* p, unsigned uses = kUsesAll) {
   if (p->num_tokens < 0) return fail(MOE_EINVAL, "num_tokens must be >= 0");
   if (p->hidden < 1) return fail(MOE_EINVAL, "hidden must be >= 1");
   if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "unknown dtype");
+  if (p->reserved != 0) return fail(MOE_EINVAL, "reserved must be 0");
+  if (p->weight_layout != MOE_LAYOUT_ROW_MAJOR && p->weight_layout != MOE_LAYOUT_BLOCKED)
+    return fail(MOE_EINVAL, "unknown weight_layout");
+  if (p->weight_layout == MOE_LAYOUT_BLOCKED && p->dtype != MOE_BF16)
+    return fail(MOE_EUNSUPPORTED, "the blocked weight layout is bf16 only");
   if (p->top_k < 1) return fail(MOE_EINVAL, "top_k must be >= 1");
   if (p->top_k > moe::kMaxTopK) return fail(MOE_EUNSUPPORTED, "top_k > %d", moe::kMaxTopK);
   const int64_t lim = (int64_t)1 << 30;
@@ -149,6 +154,7 @@ moe::GemmProblem gemm_common(const moe_problem* p) {
   g.top_k = (int32_t)p->top_k;
   g.num_pairs = (int32_t)(p->num_tokens * p->top_k);
   g.dtype = p->dtype;
+  g.weights_blocked = p->weight_layout == MOE_LAYOUT_BLOCKED;
   return g;
 }
 
@@ -198,6 +204,23 @@ int moe_align_capacity(int64_t num_pairs, int64_t num_experts, int64_t block_m, 
     return fail(MOE_EINVAL, "need num_pairs >= 0, num_experts >= 1, block_m >= 1");
   capacity(num_pairs, num_experts, block_m, max_rows, max_tiles);
   return ok();
+}
+
+int moe_pack_weights(int64_t batch, int64_t rows, int64_t cols, int32_t dtype, const void* src, void* dst,
+                     void* stream) {
+  if (dtype != MOE_BF16) return fail(MOE_EUNSUPPORTED, "the blocked weight layout is bf16 only");
+  if (batch < 0 || rows < 0 || cols < 0) return fail(MOE_EINVAL, "negative size");
+  if (rows % 8 || cols % 64) return fail(MOE_EUNSUPPORTED, "blocked weights need rows %% 8 == 0 and cols %% 64 == 0");
+  if (batch > 0 && rows > 0 && cols > 0 && batch * rows >= ((int64_t)1 << 40) / cols)
+    return fail(MOE_EUNSUPPORTED, "sizes too large");
+  const int64_t n = batch * rows * cols;
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(MOE_EINVAL, "NULL tensor");
+  if (!aligned16(src) || !aligned16(dst)) return fail(MOE_EUNSUPPORTED, "tensors must be 16-byte aligned");
+  const char *s0 = static_cast<const char*>(src), *d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + n * 2 && d0 < s0 + n * 2) return fail(MOE_EINVAL, "src and dst overlap");
+  return hip_status(moe::launch_pack_weights(src, dst, batch, rows, cols, (hipStream_t)stream), "pack_weights")
+             ?: ok();
 }
 
 int moe_get_workspace_layout(const moe_problem* p, moe_workspace_layout* layout) {

@@ -46,10 +46,16 @@ struct GemmProblem {
   int32_t block_m;
   int32_t max_tiles;
   int32_t dtype;               // MOE_F32 / MOE_BF16
+  int32_t weights_blocked;     // b in the blocked layout of moe_pack_weights (bf16 only)
 };
 
 hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s);
 hipError_t launch_down(const GemmProblem& g, hipStream_t s);
+
+// Row-major bf16 [batch, rows, cols] -> the blocked layout (rows % 8 == 0,
+// cols % 64 == 0).
+hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols,
+                               hipStream_t s);
 
 // residual_out = x (+ residual_in); normed = RMSNorm(residual_out) * weight.
 int64_t add_rmsnorm_max_hidden();

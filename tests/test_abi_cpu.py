@@ -121,3 +121,37 @@ def test_dense_mlp_and_add_rmsnorm_reject_before_any_hip_call():
     assert f(4, 64, B.MOE_BF16, None, None, fake, fake, 1e-6, other, None) == B.MOE_EINVAL
     assert f(4, 64, 7, fake, None, fake, fake, 1e-6, other, None) == B.MOE_EUNSUPPORTED
     assert f(0, 64, B.MOE_BF16, None, None, None, None, 1e-6, None, None) == 0
+
+
+def test_weight_layout_validation():
+    import torch
+    P = moe.problem
+    assert moe.moe_workspace_size(P(64, 2048, 128, 8, 768, weight_layout=B.MOE_LAYOUT_BLOCKED)) > 0
+    for bad, code in ((P(4, 64, 4, 2, 64, weight_layout=2), B.MOE_EINVAL),
+                      (P(4, 64, 4, 2, 64, dtype=torch.float32, weight_layout=B.MOE_LAYOUT_BLOCKED),
+                       B.MOE_EUNSUPPORTED)):
+        with pytest.raises(B.MoEError) as ei:
+            moe.moe_workspace_size(bad)
+        assert ei.value.code == code
+    p = P(4, 64, 4, 2, 64)
+    p.reserved = 1
+    with pytest.raises(B.MoEError) as ei:
+        moe.moe_workspace_size(p)
+    assert ei.value.code == B.MOE_EINVAL
+
+
+def test_pack_weights_rejects_before_any_hip_call():
+    lib = moe.load_library()
+    buf = ctypes.create_string_buffer(1 << 16)
+    a = ctypes.c_void_p((ctypes.addressof(buf) + 15) & ~15)
+    b = ctypes.c_void_p(a.value + 8192)
+    cases = [((1, 8, 64, B.MOE_F32, a, b), B.MOE_EUNSUPPORTED),      # fp32
+             ((1, 12, 64, B.MOE_BF16, a, b), B.MOE_EUNSUPPORTED),    # rows % 8
+             ((1, 8, 96, B.MOE_BF16, a, b), B.MOE_EUNSUPPORTED),     # cols % 64
+             ((1, 8, 64, B.MOE_BF16, None, b), B.MOE_EINVAL),        # NULL
+             ((2, 8, 64, B.MOE_BF16, a, ctypes.c_void_p(a.value + 1024)), B.MOE_EINVAL),   # overlap
+             ((1, 8, 64, B.MOE_BF16, ctypes.c_void_p(a.value + 2), b), B.MOE_EUNSUPPORTED),  # alignment
+             ((-1, 8, 64, B.MOE_BF16, a, b), B.MOE_EINVAL)]
+    for args, code in cases:
+        assert lib.moe_pack_weights(*args, None) == code, args
+    assert lib.moe_pack_weights(0, 8, 64, B.MOE_BF16, None, None, None) == B.MOE_OK   # empty: nothing enqueued

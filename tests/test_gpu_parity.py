@@ -286,3 +286,24 @@ def test_staged_calls_equal_forward():
     out2 = moe.moe_combine(y, cfg.N, cfg.top_k)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("N,H,E,k,Is", [(700, 256, 128, 8, 64), (523, 128, 64, 4, 0), (1031, 192, 160, 6, 32)])
+def test_router_tilings_bitwise_equal(N, H, E, k, Is):
+    """Batches of 512 tokens and more compute their logits in 64-token
+    tiles (x fragments shared through LDS), smaller ones in 16-token tiles;
+    a token's ids, weights and shared gate must be bit for bit the same
+    whichever batch routed it."""
+    cfg = random_case(N, H, E, k, 64, I_shared=Is, dtype="bf16", seed=3)
+    t = make_inputs(cfg, DEV)
+    gate = t["shared_gate"]
+    ids, w, sc = moe.moe_route(t["x"], t["router_w"], k, True, gate)
+    for lo, hi in ((0, 64), (N - 37, N), (511, 512)):
+        ids_s, w_s, sc_s = moe.moe_route(t["x"][lo:hi].contiguous(), t["router_w"], k, True, gate)
+        torch.cuda.synchronize()
+        assert torch.equal(ids[lo:hi], ids_s), f"ids differ in [{lo}, {hi})"
+        assert torch.equal(w[lo:hi], w_s), f"weights differ in [{lo}, {hi})"
+        if Is:
+            assert torch.equal(sc[lo:hi], sc_s), f"shared gate differs in [{lo}, {hi})"
+    h = {"x": host(t["x"]), "router_w": host(t["router_w"])}
+    compare_routing(h, cfg, ids, w)
