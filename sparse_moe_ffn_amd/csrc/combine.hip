@@ -9,7 +9,10 @@
 //
 // bf16: a thread handles 8 consecutive columns (16-byte loads of each of the
 // k rows; the k rows of a token are adjacent, so a workgroup streams one
-// contiguous block of k*H values).  fp32: one column per thread.
+// contiguous block of k*H values).  The loads of up to 8 slots are issued
+// before any of them is added, so a token costs one memory latency instead
+// of k; y is read once, so its loads are non-temporal.  fp32: one column
+// per thread.
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -26,14 +29,23 @@ __global__ __launch_bounds__(kCombineThreads) void combine_bf16_kernel(
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   const uint16_t* src = y + (int64_t)n * k * H + h0;
-  for (int j = 0; j < k; ++j) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + (int64_t)j * H);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  constexpr int kBatch = 8;
+  for (int j0 = 0; j0 < k; j0 += kBatch) {
+    u32x4_t v[kBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
-      acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+    for (int u = 0; u < kBatch; ++u)
+      if (j0 + u < k) v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + (int64_t)(j0 + u) * H));
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (j0 + u < k) {                                    // slot order
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(v[u][i] & 0xffffu));
+          acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(v[u][i] >> 16));
+        }
+      }
     }
   }
   if (ys) {
