@@ -63,11 +63,12 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
-// The same DMA marked non-temporal, for the expert weights: each weight
-// byte is read once per launch, so its lines should not push the reused
-// rows (gathered x, act) out of the caches.  Measured at 64 tokens: down
-// 78 -> 69 us, gate/up 132 -> 124 us; at 4096 tokens: gate/up 226 -> 223 us,
-// down 147 -> 135 us.
+// The same DMA marked non-temporal, for expert weights that only one row
+// tile reads: their lines should not push the reused rows (gathered x, act)
+// out of the caches.  Measured at 64 tokens: down 78 -> 69 us, gate/up
+// 132 -> 124 us; at 4096 tokens: gate/up 226 -> 223 us, down 147 -> 135 us.
+// Weights that several row tiles read (heavy experts of a skewed batch, the
+// dense products) keep the normal policy: there the hint costs 3-8%.
 __device__ __forceinline__ void dma16_nt(const uint16_t* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
@@ -229,12 +230,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
     for (int q = 0; q < A_PER_WAVE; ++q)
       if (q < kAFull || wave < kARem) dma16(src_a[q] + ko, base + (wave + NW * q) * kDmaBytes);
   };
+  // Is this weight tile read by another row tile too?  Tiles of one expert
+  // are consecutive in the grouping.
+  const bool shared_b = grouped ? ((mt > 0 && g.tile_expert[mt - 1] == expert) ||
+                                   (mt + 1 < m_tiles && g.tile_expert[mt + 1] == expert))
+                                : m_tiles > 1;
   auto issue_b = [&](int kt) {
     const uint32_t base = lds_addr(ring_b + (kt % SB) * kBStage);
     const int ko = BLK ? kpos(kt) * 8 : kpos(kt);
+    if (shared_b) {
 #pragma unroll
-    for (int q = 0; q < B_PER_WAVE; ++q)
-      if (q < kBFull || wave < kBRem) dma16_nt(src_b[q] + ko, base + (wave + NW * q) * kDmaBytes);
+      for (int q = 0; q < B_PER_WAVE; ++q)
+        if (q < kBFull || wave < kBRem) dma16(src_b[q] + ko, base + (wave + NW * q) * kDmaBytes);
+    } else {
+#pragma unroll
+      for (int q = 0; q < B_PER_WAVE; ++q)
+        if (q < kBFull || wave < kBRem) dma16_nt(src_b[q] + ko, base + (wave + NW * q) * kDmaBytes);
+    }
   };
   // Waits.  Each iteration issues the A DMAs of stage kt + SA - 1 and the
   // weight DMAs of stage kt + SB - 1; with SB > SA the A DMAs go first, with
