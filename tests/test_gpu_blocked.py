@@ -57,7 +57,7 @@ def test_forward_blocked_equals_row_major(cfg):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["decode", "prefill", "talker"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew", "talker"])
 def test_forward_blocked_equals_row_major_full_size(name):
     cfg = CONFIGS[name]
     t = make_inputs(cfg, DEV)

@@ -168,6 +168,8 @@ SMALL = [
     random_case(1200, 1024, 4, 1, 512, dtype="bf16", seed=18, norm_topk_prob=False),  # same, longer K
     random_case(700, 192, 600 // 2, 8, 64, I_shared=192, dtype="bf16", seed=14),  # E = 300: two route passes
     random_case(4100, 128, 8, 2, 64, I_shared=192, dtype="bf16", seed=19),   # shared expert on 320-row tiles
+    random_case(48, 128, 512, 32, 64, dtype="bf16", seed=20),                  # the limits: E = 512, k = 32
+    random_case(9, 128, 32, 32, 64, dtype="bf16", seed=21, norm_topk_prob=False),  # k = E = 32
     random_case(13, 33, 5, 2, 17, I_shared=9, dtype="f32", seed=11),
     random_case(64, 40, 12, 3, 24, dtype="f32", seed=12, norm_topk_prob=False),
 ]
