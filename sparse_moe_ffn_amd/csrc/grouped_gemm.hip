@@ -30,7 +30,11 @@
 // matching BN/2 up rows, and each wave holds matching gate and up columns in
 // the same lanes, so the SwiGLU is computed in registers.  Launch order puts
 // the tiles of one expert and column block next to each other on one XCD, so
-// they meet the same weight tile in that XCD's L2.
+// they meet the same weight tile in that XCD's L2.  Each expert starts its K
+// loop at its own stage (stride ROT), so concurrent workgroups spread over
+// HBM channels.  Weights are row-major or in the blocked layout of
+// moe_pack_weights (BLK: only the weight addresses differ); a weight tile that
+// one row tile reads alone is streamed with the non-temporal hint.
 //
 // fp32 kernel: plain FMA loops, any shape (used for float32 layers).
 #include <type_traits>
@@ -96,7 +100,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   else return row * BK + ((chunk ^ ((row >> 1) & 3)) << 3);
 }
 
-constexpr bool kRotateK = true;
 
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK, int ROT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
@@ -221,7 +224,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // A rows in L2.  The stride ROT is tuned per tile shape (measured).  The
   // start depends only on the expert, so every output element keeps one
   // summation order whatever the batch.
-  const int kstart = (kRotateK ? expert * ROT : 0) % nk;
+  const int kstart = (expert * ROT) % nk;
   auto kpos = [&](int kt) { const int k = kt + kstart; return (k >= nk ? k - nk : k) * BK; };
   auto issue_a = [&](int kt) {
     const uint32_t base = lds_addr(ring_a + (kt % SA) * kAStage);
