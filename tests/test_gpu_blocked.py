@@ -43,8 +43,10 @@ def forward(t, cfg, layout):
                            t["shared_w_gate_up"], t["shared_w_down"], t["shared_gate"], weight_layout=layout)
 
 
+# tile heights 16, 16, 128, 32, 64, 320 (the last also with partial column blocks)
 CASES = [random_case(1, 128, 6, 6, 64), random_case(37, 192, 16, 4, 128, I_shared=64, seed=2),
-         random_case(700, 320, 16, 4, 256, seed=4), random_case(97, 2048, 32, 8, 768)]
+         random_case(700, 320, 16, 4, 256, seed=4), random_case(97, 2048, 32, 8, 768),
+         random_case(600, 128, 16, 2, 64, seed=5), random_case(2000, 320, 8, 2, 192, I_shared=64, seed=6)]
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
