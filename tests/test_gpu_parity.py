@@ -290,17 +290,23 @@ def test_staged_calls_equal_forward():
     assert torch.equal(out, out2)
 
 
-@pytest.mark.parametrize("N,H,E,k,Is", [(700, 256, 128, 8, 64), (523, 128, 64, 4, 0), (1031, 192, 160, 6, 32)])
+@pytest.mark.parametrize("N,H,E,k,Is", [(700, 256, 128, 8, 64), (523, 128, 64, 4, 0), (1031, 192, 160, 6, 32),
+                                        (2048, 2048, 128, 8, 0), (2100, 256, 128, 8, 64),
+                                        (4099, 128, 160, 6, 32), (3000, 192, 512, 32, 0)])
 def test_router_tilings_bitwise_equal(N, H, E, k, Is):
     """Batches of 512 tokens and more compute their logits in 64-token
     tiles (x fragments shared through LDS), smaller ones in 16-token tiles;
     a token's ids, weights and shared gate must be bit for bit the same
-    whichever batch routed it."""
+    whichever batch routed it (also at the layer's own H = 2048 and at
+    E = 512)."""
     cfg = random_case(N, H, E, k, 64, I_shared=Is, dtype="bf16", seed=3)
     t = make_inputs(cfg, DEV)
     gate = t["shared_gate"]
     ids, w, sc = moe.moe_route(t["x"], t["router_w"], k, True, gate)
-    for lo, hi in ((0, 64), (N - 37, N), (511, 512)):
+    windows = [(0, 64), (N - 37, N), (511, 512)]
+    if N >= 2048:
+        windows += [(N - 1100, N - 3), (1500, 1600)]               # 64-token tiles; 16-token tiles
+    for lo, hi in windows:
         ids_s, w_s, sc_s = moe.moe_route(t["x"][lo:hi].contiguous(), t["router_w"], k, True, gate)
         torch.cuda.synchronize()
         assert torch.equal(ids[lo:hi], ids_s), f"ids differ in [{lo}, {hi})"
