@@ -101,7 +101,9 @@ def bench_workload(name, steps, warmup, torch, moe):
     # the kernels run on (torch's current stream).
     lay = moe.moe_get_workspace_layout(p)
     bm = lay["block_m"]
-    stages = ["route", "align", "gate_up", "down"] + (["shared"] if cfg.I_shared else []) + ["combine"]
+    ids_path = lay["ids_products"] == 1                # small batch: no grouping, the products scan the ids
+    stages = (["route"] + ([] if ids_path else ["align"]) + ["gate_up", "down"] + (["shared"] if cfg.I_shared else [])
+              + ["combine"])
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
     ids = torch.empty((cfg.N, cfg.top_k), dtype=torch.int32, device=dev)
     wts = torch.empty((cfg.N, cfg.top_k), dtype=torch.float32, device=dev)
@@ -110,7 +112,7 @@ def bench_workload(name, steps, warmup, torch, moe):
     align_scratch = torch.empty(max(1, moe.moe_align_scratch_size(cfg.N * cfg.top_k, cfg.E) // 4),
                                 dtype=torch.int32, device=dev)
     gr = moe.moe_align(ids.zero_(), cfg.E, bm, align_scratch)
-    act = torch.empty((gr.max_rows, cfg.I), dtype=t["x"].dtype, device=dev)
+    act = torch.empty((max(gr.max_rows, cfg.N * cfg.top_k), cfg.I), dtype=t["x"].dtype, device=dev)
     y = torch.empty((cfg.N * cfg.top_k, cfg.H), dtype=t["x"].dtype, device=dev)
     sact = torch.empty((cfg.N, cfg.I_shared), dtype=t["x"].dtype, device=dev) if cfg.I_shared else None
     sy = torch.empty((cfg.N, cfg.H), dtype=t["x"].dtype, device=dev) if cfg.I_shared else None
@@ -120,13 +122,22 @@ def bench_workload(name, steps, warmup, torch, moe):
         moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob, t["shared_gate"], ids, wts, sscale,
                       route_scratch)
         e[1].record()
-        g2 = moe.moe_align(ids, cfg.E, bm, align_scratch)
-        e[2].record()
-        moe.moe_gate_up(t["x"], tw["w_gate_up"], g2, cfg.top_k, act, weight_layout=blk)
-        e[3].record()
-        moe.moe_down(act, tw["w_down"], wts, g2, cfg.N, cfg.top_k, y, weight_layout=blk)
-        e[4].record()
-        i = 5
+        i = 2
+        g2 = None
+        if ids_path:
+            moe.moe_gate_up_ids(t["x"], tw["w_gate_up"], ids, act, weight_layout=blk)
+            e[i].record()
+            moe.moe_down_ids(act, tw["w_down"], ids, wts, y, weight_layout=blk)
+            e[i + 1].record()
+        else:
+            g2 = moe.moe_align(ids, cfg.E, bm, align_scratch)
+            e[i].record()
+            i += 1
+            moe.moe_gate_up(t["x"], tw["w_gate_up"], g2, cfg.top_k, act, weight_layout=blk)
+            e[i].record()
+            moe.moe_down(act, tw["w_down"], wts, g2, cfg.N, cfg.top_k, y, weight_layout=blk)
+            e[i + 1].record()
+        i += 2
         if cfg.I_shared:
             moe.moe_shared_expert(t["x"], tw["shared_w_gate_up"], tw["shared_w_down"], sscale, sact, sy,
                                   weight_layout=blk)
@@ -137,14 +148,14 @@ def bench_workload(name, steps, warmup, torch, moe):
         return g2
 
     for _ in range(min(warmup, 5)):
-        g2 = staged(ev[0])
+        staged(ev[0])
     torch.cuda.synchronize()
     for s in range(steps):
-        g2 = staged(ev[s])
+        staged(ev[s])
     torch.cuda.synchronize()
     stage_ms = {name_: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
                 for i, name_ in enumerate(stages)}
-    counts = g2.counts.cpu().numpy()
+    counts = moe.moe_align(ids, cfg.E, bm, align_scratch).counts.cpu().numpy()   # untimed: pairs per expert
     work = kernel_work(cfg, counts)
     ms = elapsed / steps * 1e3
     res = {
@@ -152,7 +163,7 @@ def bench_workload(name, steps, warmup, torch, moe):
         "ms_per_step_row_major": ms_row_major,
         "tflops": cfg.flops() / (ms * 1e-3) / 1e12, "stage_ms": stage_ms, "work": work,
         "hit_experts": expert_hits(counts), "counts_min_max": [int(counts.min()), int(counts.max())],
-        "block_m": bm,
+        "block_m": bm, "ids_path": ids_path,
     }
     res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFLOPS
     weight_bytes = res["hit_experts"] * 3 * cfg.I * cfg.H * 2 + cfg.I_shared * 3 * cfg.H * 2
@@ -289,7 +300,8 @@ def roofline_for(res):
     w = res["work"][kern]
     gbs = w["bytes"] / dur_s / 1e9
     tfs = w["flops"] / dur_s / 1e12
-    common = {"kernel": f"grouped_gemm_bf16 gate_up (SwiGLU epilogue), block_m {res['block_m']}, blocked weights",
+    tiles = "16-row passes over the top-k ids" if res["ids_path"] else f"block_m {res['block_m']}"
+    common = {"kernel": f"grouped_gemm_bf16 gate_up (SwiGLU epilogue), {tiles}, blocked weights",
               "traffic": measured_traffic(cfg.name), "avg_launch_ms": round(res["stage_ms"][kern], 4),
               "algorithmic_bytes_per_launch": w["bytes"], "algorithmic_flops_per_launch": w["flops"],
               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}

@@ -94,6 +94,8 @@ typedef struct moe_workspace_layout {
   int64_t block_m;         /* rows per grouped-GEMM tile */
   int64_t max_rows;        /* capacity of sorted_pairs / act rows */
   int64_t max_tiles;       /* capacity of tile_expert / tile_rows */
+  int64_t ids_products;    /* 1: moe_forward runs moe_gate_up_ids / moe_down_ids
+                              (no grouping; act rows are pair indices) */
   size_t route_scratch, topk_ids, topk_w, shared_scale;
   size_t counts, offsets, order, sorted_pairs, tile_expert, tile_rows, num_tiles, align_scratch;
   size_t act, y, shared_act, shared_y;
@@ -210,6 +212,24 @@ int moe_down(const moe_problem* p, const void* act, const void* w_down,
              const int32_t* num_tiles, int64_t block_m, int64_t max_tiles,
              void* y, void* stream);
 
+/* The same two products for small batches without a grouping: each
+ * (expert, column block) workgroup finds the pairs p with topk_ids[p] == e
+ * itself, in increasing p (the stable order of M03 逐步图 steps 1-2), and
+ * runs them 16 rows at a time.  act and y are indexed by the pair:
+ *   moe_gate_up_ids:  act[p, i] = silu(x[p / k] . Wg[e, i]) * (x[p / k] . Wu[e, i])
+ *   moe_down_ids:     y[p, h]   = topk_w[p] * (act[p] . Wd[e, h])
+ * with e = topk_ids[p];  act [N*k, I] and y [N*k, H] dtype, every row written
+ * once.  Each row is computed with the instructions and K order of the
+ * grouped products at block_m 16, so act[p] and y[p] are bit for bit the
+ * grouped results for the same pair.  moe_forward uses them when the
+ * grouped path would take 16-row tiles.  bf16 only, with 4 <= N*k <= 1024
+ * and N*k a multiple of 4 (otherwise MOE_EUNSUPPORTED); topk_ids [N, k]
+ * int32 in [0, E), 16-byte aligned; no scratch. */
+int moe_gate_up_ids(const moe_problem* p, const void* x, const void* w_gate_up,
+                    const int32_t* topk_ids, void* act, void* stream);
+int moe_down_ids(const moe_problem* p, const void* act, const void* w_down,
+                 const int32_t* topk_ids, const float* topk_w, void* y, void* stream);
+
 /* Shared expert (M03 题面速览, talker's shared expert; "Qwen3.5 推理全流程"
  * 2.5B formula, second term): dense over all N tokens,
  *   shared_act[n] = silu(x[n] Wg_s^T) * (x[n] Wu_s^T)        [N, I_s]
@@ -261,7 +281,10 @@ int moe_combine(const moe_problem* p, const void* y, const void* shared_y,
                 void* out, void* stream);
 
 /* The whole block: moe_route, moe_align, moe_gate_up, moe_down,
- * [moe_shared_expert], moe_combine on one stream, in that order, with every
+ * [moe_shared_expert], moe_combine on one stream, in that order (for batches
+ * the grouped products would run in 16-row tiles and that moe_gate_up_ids
+ * takes: moe_route, moe_gate_up_ids, moe_down_ids, [moe_shared_expert],
+ * moe_combine, with the same output bit for bit), with every
  * intermediate in `workspace` (moe_workspace_size bytes, 256-byte aligned,
  * laid out as moe_get_workspace_layout says).  shared_w_gate_up == NULL means
  * no shared expert (then shared_w_down and shared_gate are ignored and

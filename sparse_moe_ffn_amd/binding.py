@@ -41,7 +41,8 @@ class MoEProblem(ctypes.Structure):
 
 
 class MoEWorkspaceLayout(ctypes.Structure):
-    _fields_ = [("block_m", ctypes.c_int64), ("max_rows", ctypes.c_int64), ("max_tiles", ctypes.c_int64)] + [
+    _fields_ = [("block_m", ctypes.c_int64), ("max_rows", ctypes.c_int64), ("max_tiles", ctypes.c_int64),
+                ("ids_products", ctypes.c_int64)] + [
         (n, ctypes.c_size_t) for n in ("route_scratch", "topk_ids", "topk_w", "shared_scale", "counts", "offsets",
                                        "order",
                                        "sorted_pairs", "tile_expert", "tile_rows", "num_tiles", "align_scratch",
@@ -72,6 +73,8 @@ def load_library() -> ctypes.CDLL:
             "moe_align_scratch_size": [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)],
             "moe_gate_up": [PP, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P],
             "moe_down": [PP, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _P, _P],
+            "moe_gate_up_ids": [PP, _P, _P, _P, _P, _P],
+            "moe_down_ids": [PP, _P, _P, _P, _P, _P, _P],
             "moe_shared_expert": [PP, _P, _P, _P, _P, _P, _P, _P],
             "moe_combine": [PP, _P, _P, _P, _P],
             "moe_forward": [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -279,6 +282,47 @@ def moe_down(act, w_down, topk_w, grouping: Grouping, num_tokens: int, top_k: in
                                        _ptr(grouping.sorted_pairs), _ptr(grouping.tile_expert),
                                        _ptr(grouping.tile_rows), _ptr(grouping.num_tiles), grouping.block_m,
                                        grouping.max_tiles, _ptr(y), _stream(dev)))
+    return y
+
+
+def moe_gate_up_ids(x, w_gate_up, topk_ids, act=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
+    """act [N*k, I] in x.dtype, indexed by pair: act[p] = SwiGLU of x[p / k]
+    through expert topk_ids[p] (no grouping needed; bf16, 4 <= N*k <= 1024)."""
+    x = _gpu(x, "x")
+    dev = x.device
+    w_gate_up = _gpu(w_gate_up, "w_gate_up", x.dtype, dev)
+    topk_ids = _gpu(topk_ids, "topk_ids", torch.int32, dev)
+    N, H = x.shape
+    E, two_i, _ = w_gate_up.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != N:
+        raise ValueError("topk_ids must be [N, k]")
+    k = topk_ids.shape[1]
+    p = problem(N, H, E, k, two_i // 2, 0, x.dtype, weight_layout=weight_layout)
+    if act is None:
+        act = torch.empty((N * k, two_i // 2), dtype=x.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_gate_up_ids(ctypes.byref(p), _ptr(x), _ptr(w_gate_up), _ptr(topk_ids), _ptr(act),
+                                              _stream(dev)))
+    return act
+
+
+def moe_down_ids(act, w_down, topk_ids, topk_w, y=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
+    """y [N*k, H] in act.dtype: y[p] = topk_w[p] * (act[p] . w_down[topk_ids[p]]^T)."""
+    act = _gpu(act, "act")
+    dev = act.device
+    w_down = _gpu(w_down, "w_down", act.dtype, dev)
+    topk_ids = _gpu(topk_ids, "topk_ids", torch.int32, dev)
+    topk_w = _gpu(topk_w, "topk_w", torch.float32, dev)
+    E, H, I = w_down.shape
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [N, k]")
+    N, k = topk_ids.shape
+    p = problem(N, H, E, k, I, 0, act.dtype, weight_layout=weight_layout)
+    if y is None:
+        y = torch.empty((N * k, H), dtype=act.dtype, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_down_ids(ctypes.byref(p), _ptr(act), _ptr(w_down), _ptr(topk_ids), _ptr(topk_w),
+                                           _ptr(y), _stream(dev)))
     return y
 
 

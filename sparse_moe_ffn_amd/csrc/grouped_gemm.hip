@@ -20,6 +20,15 @@
 // tiles; workgroups past the device-side tile count return at once, so the
 // host never reads the count.
 //
+// Scan mode (small batches, 16-row tiles): no align kernel.  Workgroup
+// (expert e, column block) copies the top-k ids into its A ring while its
+// first weight stages load, and lists the pairs p with ids[p] == e in
+// increasing p: the align kernel's stable order.  It then runs those rows 16
+// at a time (one pass for nearly every expert at decode sizes), reading act
+// and writing act / y at the pair index p.  A row's products are the same
+// instructions in the same K order as in the grouped tiles, so act, y and the
+// block's output are bit for bit those of the grouped path.
+//
 // bf16 kernel (gfx950): C = A . B^T with A gathered rows [BM, K] and B the
 // expert's weight rows [BN, K], both K-contiguous.  64-wide K steps go from
 // global memory straight into LDS (16-byte-per-lane DMA), 2-3 steps ahead of
@@ -101,7 +110,7 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK, int ROT>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK, int ROT, bool SCAN>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(!BLK || BK == 64, "blocked weights come in 64-column blocks, one per stage");
@@ -134,11 +143,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   uint16_t* const ring_a = smem;
   uint16_t* const ring_b = smem + SA * kAStage;
   // Down: output row (pair index) and routing weight of every tile row,
-  // loaded once at the start so the epilogue reads them from LDS.
-  __shared__ int32_t ep_row[MODE == kDown ? BM : 1];
-  __shared__ float ep_scale[MODE == kDown ? BM : 1];
+  // loaded once at the start so the epilogue reads them from LDS.  Scan mode
+  // (16-row tiles only) keeps the current pass's pairs in ep_row (down's
+  // table holds the same pairs) and, during the scan, the per-wave match
+  // counts in ep_scale (filled only afterwards).
+  static_assert(!SCAN || (BM == 16 && NW <= BM), "scan mode runs 16-row passes");
+  constexpr bool scan = SCAN;
+  __shared__ int32_t ep_row[(MODE == kDown || SCAN) ? BM : 1];
+  __shared__ float ep_scale[(MODE == kDown || SCAN) ? BM : 1];
+  int32_t* const scan_rows = ep_row;
+  int32_t* const scan_count = reinterpret_cast<int32_t*>(ep_scale);
 
-  const bool grouped = g.sorted_pairs != nullptr;
+  const bool grouped = !SCAN && g.sorted_pairs != nullptr;
   const int half = BN / 2;
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + half - 1) / half : (g.n_out + BN - 1) / BN;
   // Workgroups past the real number of tiles leave at once; the others are
@@ -146,7 +162,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // column blocks of a few consecutive row tiles together: they share the
   // gathered A rows and (row tiles of one expert) the expert's weights in
   // that XCD's L2.
-  const int m_tiles = grouped ? *g.num_tiles : (g.dense_rows + BM - 1) / BM;
+  const int m_tiles = grouped ? *g.num_tiles : (scan ? g.num_experts : (g.dense_rows + BM - 1) / BM);
   const int n_blocks = m_tiles * n_tiles_n;
   if ((int)blockIdx.x >= n_blocks) return;
   const int logical = xcd_swizzle(blockIdx.x, n_blocks);
@@ -156,6 +172,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   if (grouped) {
     rows_valid = g.tile_rows[mt];
     expert = g.tile_expert[mt];
+  } else if (scan) {
+    rows_valid = 0;                                    // set by each pass
+    expert = mt;
   } else {
     rows_valid = min(BM, g.dense_rows - mt * BM);
     expert = 0;
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // are consecutive in the grouping.
   const bool shared_b = grouped ? ((mt > 0 && g.tile_expert[mt - 1] == expert) ||
                                    (mt + 1 < m_tiles && g.tile_expert[mt + 1] == expert))
-                                : m_tiles > 1;
+                                : (!scan && m_tiles > 1);
   auto issue_b = [&](int kt) {
     const uint32_t base = lds_addr(ring_b + (kt % SB) * kBStage);
     const int ko = BLK ? kpos(kt) * 8 : kpos(kt);
@@ -293,7 +312,85 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
     else wait_counts(kt, AF{}, BF{});
   };
 
+  // Scan mode: copy the ids into the A ring (free until the first A stage),
+  // issue this pass's first weight stages, wait for the ids only (they are
+  // older than the weight DMAs), then list the expert's pairs with ranks
+  // [c0, c0 + BM) into scan_rows.  Thread t looks at ids [8t, 8t + 8), so the
+  // ranks follow the pair index.  Returns the expert's number of pairs.
+  auto scan_pass = [&](int c0) -> int {
+    if constexpr (SCAN) {
+      static_assert(SA * kAStage * 2 >= kScanMaxPairs * 4 && 8 * 64 * NW >= kScanMaxPairs,
+                    "the ids must fit the A ring, 8 per thread");
+      const int P = g.num_pairs;                       // 4 <= P <= kScanMaxPairs, P % 4 == 0 (launcher)
+      const uint32_t ids_lds = lds_addr(ring_a);
+      for (int gi = wave; gi < (P + 255) / 256; gi += NW)
+        dma16(reinterpret_cast<const uint16_t*>(g.topk_ids + min(gi * 256 + lane * 4, P - 4)),
+              ids_lds + gi * kDmaBytes);
+      for (int st = 0; st < min(SB - 1, nk); ++st) issue_b(st);
+      if (nk >= SB - 1) {
+        if (wave < kBRem) wait_vmcnt<(SB - 1) * (kBFull + 1)>();
+        else wait_vmcnt<(SB - 1) * kBFull>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __syncthreads();
+      const int32_t* ids = reinterpret_cast<const int32_t*>(ring_a);
+      const int p0 = threadIdx.x * 8;
+      int c = 0;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p0 + u < P && ids[p0 + u] == expert) {
+          bits |= 1u << u;
+          ++c;
+        }
+      int incl = c;                                    // inclusive prefix over the wave
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+      }
+      if (lane == 63) scan_count[wave] = incl;
+      __syncthreads();
+      int rank = incl - c, total = 0;
+      for (int w = 0; w < NW; ++w) {
+        const int t = scan_count[w];
+        if (w < wave) rank += t;
+        total += t;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if ((bits >> u) & 1u) {
+          const int r = rank++ - c0;
+          if (r >= 0 && r < BM) scan_rows[r] = p0 + u;
+        }
+      __syncthreads();                                 // scan_rows written; the ids are no longer read
+      rows_valid = min(BM, max(0, total - c0));
+      return total;
+    }
+    return 0;
+  };
+
   floatx4 acc[TM][TN];
+  // One pass over the tile's rows (scan mode: one per BM pairs of the expert).
+  for (int c0 = 0, scan_total = 0;; c0 += BM) {
+  if constexpr (SCAN) {
+    scan_total = scan_pass(c0);
+    if (c0 >= scan_total) {                            // nothing (left) for this expert
+      wait_vmcnt<0>();                                 // the weight stages have landed
+      break;
+    }
+    // Sources of this lane's A pieces: the pass's pairs (rows past them read pair 0).
+#pragma unroll
+    for (int q = 0; q < A_PER_WAVE; ++q) {
+      src_a[q] = A;
+      if (wave + NW * q >= NA_DMA) continue;
+      const int r = (wave + NW * q) * kRowsPerDma + lane / kCpr;
+      const int chunk = (swz<BK>(r, lane % kCpr) - r * BK) >> 3;
+      const int pr = r < rows_valid ? scan_rows[r] : 0;
+      src_a[q] = A + (int64_t)((MODE == kGateUp) ? pr / g.top_k : pr) * K + chunk * 8;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -326,7 +423,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
         int prow = -1;
         float sc = 0.0f;
         if (r < rows_valid) {
-          prow = grouped ? g.sorted_pairs[row0 + r] : row0 + r;
+          prow = grouped ? g.sorted_pairs[row0 + r] : (scan ? scan_rows[r] : row0 + r);
           sc = g.scale ? g.scale[prow] : 1.0f;
         }
         ep_row[r] = prow;
@@ -335,7 +432,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
     }
   };
   auto main_loop = [&](auto compute) {
-    for (int s = 0; s < min(SB - 1, nk); ++s) issue_b(s);
+    if (!scan)                                         // scan mode: issued by scan_pass
+      for (int s = 0; s < min(SB - 1, nk); ++s) issue_b(s);
     for (int s = 0; s < min(SA - 1, nk); ++s) issue_a(s);
     fill_tables();                                     // in the shadow of the first stage's loads
     for (int kt = 0; kt < nk; ++kt) {
@@ -433,11 +531,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
       const int rl = c / CPR, j = c % CPR;
       if (col0 + j * 8 >= g.n_out) continue;
       const int r = e0 + rl;
-      const int64_t orow = (MODE == kGateUp) ? row0 + r : ep_row[r];
+      const int64_t orow = (MODE == kGateUp) ? (scan ? scan_rows[r] : row0 + r) : ep_row[r];
       *reinterpret_cast<uint4*>(C + orow * g.n_out + col0 + j * 8) =
           *reinterpret_cast<const uint4*>(so + rl * OUT_LD + j * 8);
     }
   }
+  if constexpr (!SCAN) {
+    break;
+  } else {
+    if (c0 + BM >= scan_total) break;
+    __syncthreads();                                   // the staged output is read; the next pass reuses the LDS
+  }
+  }  // passes
 }
 
 // ---------------------------------------------------------------- float32
@@ -525,17 +630,36 @@ static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
   const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
   if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(64 * WAVES_M * WAVES_N);
+  const bool scan = g.topk_ids != nullptr && g.sorted_pairs == nullptr;
+  if constexpr (BM == 16) {
+    if (scan) {
+      if (g.weights_blocked)
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true, ROT, true>),
+                           grid, block, 0, s, g);
+      else
+        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false, ROT, true>),
+                           grid, block, 0, s, g);
+      return hipGetLastError();
+    }
+  } else {
+    if (scan) return hipErrorInvalidValue;
+  }
   if (g.weights_blocked)
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true, ROT>),
-                       dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true, ROT, false>),
+                       grid, block, 0, s, g);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false, ROT>),
-                       dim3((unsigned)blocks), dim3(64 * WAVES_M * WAVES_N), 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false, ROT, false>),
+                       grid, block, 0, s, g);
   return hipGetLastError();
 }
 
 template <int MODE>
 static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
+  if (g.topk_ids && !g.sorted_pairs &&
+      (g.dtype != MOE_BF16 || g.block_m != 16 || g.max_tiles != g.num_experts || g.num_pairs < 4 ||
+       g.num_pairs > kScanMaxPairs || g.num_pairs % 4 != 0))
+    return hipErrorInvalidValue;                       // outside what scan mode is built for
   if (g.dtype == MOE_F32) {
     const dim3 grid(g.max_tiles, (g.n_out + kF32Cols - 1) / kF32Cols);
     if (grid.x == 0) return hipSuccess;

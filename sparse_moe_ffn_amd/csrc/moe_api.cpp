@@ -116,12 +116,23 @@ void capacity(int64_t pairs, int64_t experts, int64_t bm, int64_t* rows, int64_t
   *rows = t * bm;
 }
 
+// moe_forward's small-batch schedule: the grouped products scan the top-k
+// ids themselves instead of reading an align table (16-row tiles, and the
+// ids must fit the tile's A ring).
+bool ids_supported(const moe_problem* p) {
+  const int64_t P = p->num_tokens * p->top_k;
+  return p->dtype == MOE_BF16 && P >= 4 && P <= moe::kScanMaxPairs && P % 4 == 0;
+}
+
+bool scan_mode(const moe_problem* p, const moe_workspace_layout& L) { return L.block_m == 16 && ids_supported(p); }
+
 void layout_of(const moe_problem* p, moe_workspace_layout* L) {
   memset(L, 0, sizeof(*L));
   const int64_t N = p->num_tokens, P = N * p->top_k, E = p->num_experts;
   const size_t es = elt_size(p->dtype);
   L->block_m = choose_block_m(p);
   capacity(P, E, L->block_m, &L->max_rows, &L->max_tiles);
+  L->ids_products = scan_mode(p, *L) ? 1 : 0;
   size_t off = 0;
   auto region = [&](size_t bytes) {
     off = (off + 255) & ~(size_t)255;
@@ -155,6 +166,16 @@ moe::GemmProblem gemm_common(const moe_problem* p) {
   g.num_pairs = (int32_t)(p->num_tokens * p->top_k);
   g.dtype = p->dtype;
   g.weights_blocked = p->weight_layout == MOE_LAYOUT_BLOCKED;
+  return g;
+}
+
+// Gate/up or down in scan mode (arguments checked by the caller).
+moe::GemmProblem ids_problem(const moe_problem* p, const int32_t* topk_ids) {
+  moe::GemmProblem g = gemm_common(p);
+  g.topk_ids = topk_ids;
+  g.num_experts = (int32_t)p->num_experts;
+  g.block_m = 16;
+  g.max_tiles = (int32_t)p->num_experts;
   return g;
 }
 
@@ -339,6 +360,45 @@ int moe_down(const moe_problem* p, const void* act, const void* w_down, const fl
   return hip_status(moe::launch_down(g, (hipStream_t)stream), "down") ?: ok();
 }
 
+int moe_gate_up_ids(const moe_problem* p, const void* x, const void* w_gate_up, const int32_t* topk_ids,
+                    void* act, void* stream) {
+  if (int rc = check_problem(p, kUsesExperts | kUsesInter)) return rc;
+  if (p->num_tokens == 0) return ok();
+  if (!x || !w_gate_up || !topk_ids || !act) return fail(MOE_EINVAL, "NULL tensor");
+  if (!ids_supported(p))
+    return fail(MOE_EUNSUPPORTED, "needs bf16 and 4 <= N*k <= %d with N*k a multiple of 4", moe::kScanMaxPairs);
+  if (!aligned16(topk_ids)) return fail(MOE_EUNSUPPORTED, "topk_ids must be 16-byte aligned");
+  if (int rc = check_ptrs_bf16(p, {x, w_gate_up, act})) return rc;
+  moe::GemmProblem g = ids_problem(p, topk_ids);
+  g.a = x;
+  g.b = w_gate_up;
+  g.c = act;
+  g.expert_stride = 2 * p->inter * p->hidden;
+  g.K = (int32_t)p->hidden;
+  g.n_out = (int32_t)p->inter;
+  return hip_status(moe::launch_gate_up(g, (hipStream_t)stream), "gate_up_ids") ?: ok();
+}
+
+int moe_down_ids(const moe_problem* p, const void* act, const void* w_down, const int32_t* topk_ids,
+                 const float* topk_w, void* y, void* stream) {
+  if (int rc = check_problem(p, kUsesExperts | kUsesInter)) return rc;
+  if (p->num_tokens == 0) return ok();
+  if (!act || !w_down || !topk_ids || !topk_w || !y) return fail(MOE_EINVAL, "NULL tensor");
+  if (!ids_supported(p))
+    return fail(MOE_EUNSUPPORTED, "needs bf16 and 4 <= N*k <= %d with N*k a multiple of 4", moe::kScanMaxPairs);
+  if (!aligned16(topk_ids)) return fail(MOE_EUNSUPPORTED, "topk_ids must be 16-byte aligned");
+  if (int rc = check_ptrs_bf16(p, {act, w_down, y})) return rc;
+  moe::GemmProblem g = ids_problem(p, topk_ids);
+  g.a = act;
+  g.b = w_down;
+  g.c = y;
+  g.scale = topk_w;
+  g.expert_stride = p->hidden * p->inter;
+  g.K = (int32_t)p->inter;
+  g.n_out = (int32_t)p->hidden;
+  return hip_status(moe::launch_down(g, (hipStream_t)stream), "down_ids") ?: ok();
+}
+
 int moe_shared_expert(const moe_problem* p, const void* x, const void* shared_w_gate_up,
                       const void* shared_w_down, const float* shared_scale, void* shared_act,
                       void* shared_y, void* stream) {
@@ -418,20 +478,27 @@ int moe_forward(const moe_problem* p, const void* x, const void* router_w, const
   if (int rc = moe_route(p, x, router_w, shared ? shared_gate : nullptr, ids, w, sscale,
                          (float*)at(L.route_scratch), stream))
     return rc;
-  int32_t* sorted = (int32_t*)at(L.sorted_pairs);
-  int32_t* texp = (int32_t*)at(L.tile_expert);
-  int32_t* trows = (int32_t*)at(L.tile_rows);
-  int32_t* ntiles = (int32_t*)at(L.num_tiles);
-  if (int rc = moe_align(ids, p->num_tokens, p->top_k, p->num_experts, L.block_m, (int32_t*)at(L.counts),
-                         (int32_t*)at(L.offsets), (int32_t*)at(L.order), sorted, texp, trows, ntiles,
-                         (int32_t*)at(L.align_scratch), stream))
-    return rc;
-  if (int rc = moe_gate_up(p, x, w_gate_up, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
-                           at(L.act), stream))
-    return rc;
-  if (int rc = moe_down(p, at(L.act), w_down, w, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
-                        at(L.y), stream))
-    return rc;
+  if (L.ids_products) {
+    // Small batch: the products find their expert's pairs themselves (no
+    // align launch); act and y rows are pair indices.
+    if (int rc = moe_gate_up_ids(p, x, w_gate_up, ids, at(L.act), stream)) return rc;
+    if (int rc = moe_down_ids(p, at(L.act), w_down, ids, w, at(L.y), stream)) return rc;
+  } else {
+    int32_t* sorted = (int32_t*)at(L.sorted_pairs);
+    int32_t* texp = (int32_t*)at(L.tile_expert);
+    int32_t* trows = (int32_t*)at(L.tile_rows);
+    int32_t* ntiles = (int32_t*)at(L.num_tiles);
+    if (int rc = moe_align(ids, p->num_tokens, p->top_k, p->num_experts, L.block_m, (int32_t*)at(L.counts),
+                           (int32_t*)at(L.offsets), (int32_t*)at(L.order), sorted, texp, trows, ntiles,
+                           (int32_t*)at(L.align_scratch), stream))
+      return rc;
+    if (int rc = moe_gate_up(p, x, w_gate_up, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
+                             at(L.act), stream))
+      return rc;
+    if (int rc = moe_down(p, at(L.act), w_down, w, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
+                          at(L.y), stream))
+      return rc;
+  }
   if (shared) {
     if (int rc = moe_shared_expert(p, x, shared_w_gate_up, shared_w_down, sscale, at(L.shared_act),
                                    at(L.shared_y), stream))

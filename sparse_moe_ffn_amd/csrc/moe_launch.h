@@ -47,7 +47,15 @@ struct GemmProblem {
   int32_t max_tiles;
   int32_t dtype;               // MOE_F32 / MOE_BF16
   int32_t weights_blocked;     // b in the blocked layout of moe_pack_weights (bf16 only)
+  // Scan mode (sorted_pairs == nullptr, topk_ids != nullptr; bf16, block_m 16,
+  // max_tiles = num_experts, 4 <= num_pairs <= kScanMaxPairs, num_pairs % 4 == 0):
+  // workgroup e lists the pairs with topk_ids[p] == e itself; act and y rows
+  // are pair indices.
+  const int32_t* topk_ids;
+  int32_t num_experts;
 };
+
+constexpr int kScanMaxPairs = 1024;   // ids that fit the 16-row tile's A ring (and 8 per thread)
 
 hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s);
 hipError_t launch_down(const GemmProblem& g, hipStream_t s);

@@ -155,3 +155,25 @@ def test_pack_weights_rejects_before_any_hip_call():
     for args, code in cases:
         assert lib.moe_pack_weights(*args, None) == code, args
     assert lib.moe_pack_weights(0, 8, 64, B.MOE_BF16, None, None, None) == B.MOE_OK   # empty: nothing enqueued
+
+
+def test_ids_products_reject_before_any_hip_call():
+    """moe_gate_up_ids / moe_down_ids: bf16, 4 <= N*k <= 1024, N*k % 4 == 0,
+    16-byte aligned ids; every rejection happens before a HIP call (no GPU here)."""
+    import torch
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    ok_p = moe.problem(64, 128, 16, 8, 64)
+    for p, code in ((moe.problem(64, 128, 16, 8, 64, dtype=torch.float32), B.MOE_EUNSUPPORTED),
+                    (moe.problem(129, 128, 16, 8, 64), B.MOE_EUNSUPPORTED),      # 1032 pairs
+                    (moe.problem(3, 128, 16, 3, 64), B.MOE_EUNSUPPORTED),        # 9 pairs
+                    (moe.problem(1, 128, 16, 2, 64), B.MOE_EUNSUPPORTED)):       # 2 pairs
+        assert lib.moe_gate_up_ids(ctypes.byref(p), fake, fake, fake, fake, None) == code
+        assert lib.moe_down_ids(ctypes.byref(p), fake, fake, fake, fake, fake, None) == code
+    unaligned = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.moe_gate_up_ids(ctypes.byref(ok_p), fake, fake, unaligned, fake, None) == B.MOE_EUNSUPPORTED
+    assert lib.moe_down_ids(ctypes.byref(ok_p), fake, fake, unaligned, fake, fake, None) == B.MOE_EUNSUPPORTED
+    assert lib.moe_gate_up_ids(ctypes.byref(ok_p), fake, fake, None, fake, None) == B.MOE_EINVAL
+    assert lib.moe_down_ids(ctypes.byref(ok_p), fake, fake, fake, None, fake, None) == B.MOE_EINVAL
+    p0 = moe.problem(0, 128, 16, 8, 64)
+    assert lib.moe_gate_up_ids(ctypes.byref(p0), None, None, None, None, None) == 0
