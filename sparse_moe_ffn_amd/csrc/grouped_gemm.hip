@@ -624,32 +624,19 @@ hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_
 
 // ROT: K-start stride.  Both weight layouts use the same stride, so they
 // sum in the same order and give bit for bit the same results.
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = 7>
+// SCAN: the small-batch products that scan the top-k ids (16-row tiles).
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = 7, bool SCAN = false>
 static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
   if (g.block_m != BM) return hipErrorInvalidValue;   // tiles must be laid out for this height
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
   const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(64 * WAVES_M * WAVES_N);
-  const bool scan = g.topk_ids != nullptr && g.sorted_pairs == nullptr;
-  if constexpr (BM == 16) {
-    if (scan) {
-      if (g.weights_blocked)
-        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true, ROT, true>),
-                           grid, block, 0, s, g);
-      else
-        hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false, ROT, true>),
-                           grid, block, 0, s, g);
-      return hipGetLastError();
-    }
-  } else {
-    if (scan) return hipErrorInvalidValue;
-  }
   if (g.weights_blocked)
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true, ROT, false>),
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true, ROT, SCAN>),
                        grid, block, 0, s, g);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false, ROT, false>),
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false, ROT, SCAN>),
                        grid, block, 0, s, g);
   return hipGetLastError();
 }
@@ -665,6 +652,23 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     if (grid.x == 0) return hipSuccess;
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<MODE>, grid, dim3(kF32Threads), 0, s, g);
     return hipGetLastError();
+  }
+  if (g.topk_ids && !g.sorted_pairs) {
+    // Scan mode: one workgroup per (expert, column block) whatever the
+    // routing, so the tile width sets the number of workgroup rounds
+    // directly.  Measured at 32 / 64 / 128 tokens (H=2048, E=128, top-8,
+    // blocked weights), against 16x128 tiles for both products:
+    //   gate/up 16x256 (4 waves, 3 weight slots): 108.3 / 118.3 / 130.7 us
+    //     against 109.7 / 118.7 / 132.9;
+    //   down 16x256 (8 waves, 2 slots): 55.1 / 60.1 / 70.5 us against
+    //     59.2 / 62.3 / 64.5: better while experts average at most 4 pairs
+    //     (then nearly all take one 16-row pass), worse at 8, where the odd
+    //     expert with a second pass ends the last of exactly two rounds late.
+    // Results are the same bit for bit: the tile width does not change any
+    // row's arithmetic.
+    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, 5, true>(g, s);
+    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 8, 2, 2, MODE, 5, true>(g, s);
+    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 5, true>(g, s);
   }
   switch (g.block_m) {
     case 16:   // decode.  K-start stride 5: gate/up at 64 tokens 130 -> 127 us with blocked
