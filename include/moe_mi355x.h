@@ -224,7 +224,9 @@ int moe_down(const moe_problem* p, const void* act, const void* w_down,
  * grouped results for the same pair.  moe_forward uses them when the
  * grouped path would take 16-row tiles.  bf16 only, with 4 <= N*k <= 1024
  * and N*k a multiple of 4 (otherwise MOE_EUNSUPPORTED); topk_ids [N, k]
- * int32 in [0, E), 16-byte aligned; no scratch. */
+ * int32, 16-byte aligned; an id outside [0, E) matches no expert, and the
+ * rows of its pair are left unwritten (as moe_align drops such pairs); no
+ * scratch. */
 int moe_gate_up_ids(const moe_problem* p, const void* x, const void* w_gate_up,
                     const int32_t* topk_ids, void* act, void* stream);
 int moe_down_ids(const moe_problem* p, const void* act, const void* w_down,

@@ -83,3 +83,40 @@ def test_forward_takes_the_ids_products_bitwise():
     ref = moe.moe_combine(y, cfg.N, cfg.top_k, sy)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_out_of_range_ids_match_no_expert():
+    """Ids outside [0, E) (negative or >= E) match no expert: their pairs'
+    rows stay as they were, every other row is the grouped result (moe_align
+    drops the same pairs)."""
+    cfg = random_case(64, 256, 32, 8, 128, seed=48)
+    t = make_inputs(cfg, DEV)
+    ids, w, _ = moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    bad = ids.clone()
+    bad[3, 1] = -7
+    bad[10, 0] = cfg.E
+    bad[63, 7] = 1 << 30
+    P = cfg.N * cfg.top_k
+    dropped = torch.zeros(P, dtype=torch.bool)
+    for n, j in ((3, 1), (10, 0), (63, 7)):
+        dropped[n * cfg.top_k + j] = True
+    gr = moe.moe_align(bad, cfg.E, 16)
+    act_g = moe.moe_gate_up(t["x"], t["w_gate_up"], gr, cfg.top_k)
+    y_g = moe.moe_down(act_g, t["w_down"], w, gr, cfg.N, cfg.top_k)
+    act_i = torch.full((P, cfg.I), 7.0, dtype=t["x"].dtype, device=DEV)
+    y_i = torch.full((P, cfg.H), 7.0, dtype=t["x"].dtype, device=DEV)
+    moe.moe_gate_up_ids(t["x"], t["w_gate_up"], bad, act_i)
+    moe.moe_down_ids(act_i, t["w_down"], bad, w, y_i)
+    torch.cuda.synchronize()
+    assert int(gr.counts.sum().item()) == P - 3
+    rows = int(gr.num_tiles.item()) * 16
+    sp = gr.sorted_pairs[:rows].long().cpu()
+    real = sp < P
+    keep = ~dropped
+    rows_of_pair = torch.full((P,), -1, dtype=torch.long)
+    rows_of_pair[sp[real]] = torch.nonzero(real).reshape(-1)
+    assert bool((rows_of_pair[keep] >= 0).all()) and bool((rows_of_pair[dropped] == -1).all())
+    kd = keep.to(DEV)
+    assert torch.equal(act_i[kd].view(torch.int16), act_g[rows_of_pair[keep].to(DEV)].view(torch.int16))
+    assert torch.equal(y_i[kd].view(torch.int16), y_g[kd].view(torch.int16))
+    assert bool((act_i[~kd] == 7.0).all()) and bool((y_i[~kd] == 7.0).all())
