@@ -315,3 +315,25 @@ def test_router_tilings_bitwise_equal(N, H, E, k, Is):
             assert torch.equal(sc[lo:hi], sc_s), f"shared gate differs in [{lo}, {hi})"
     h = {"x": host(t["x"]), "router_w": host(t["router_w"])}
     compare_routing(h, cfg, ids, w)
+
+
+@pytest.mark.parametrize("N,H,E,k,I,Is", [(700, 256, 64, 8, 128, 0), (2100, 128, 16, 4, 64, 64)])
+def test_forward_multichunk_grouping_equals_staged(N, H, E, k, I, Is):
+    """Groupings of several 4096-pair chunks (count, scan and scatter
+    launches): moe_forward must equal the staged public calls bit for bit."""
+    cfg = random_case(N, H, E, k, I, I_shared=Is, dtype="bf16", seed=13)
+    t = make_inputs(cfg, DEV)
+    out = run_forward(t, cfg)
+    lay = moe.moe_get_workspace_layout(moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], k,
+                                                        cfg.norm_topk_prob, t["shared_w_gate_up"]))
+    assert lay["ids_products"] == 0 and N * k > 4096
+    ids, w, sc = moe.moe_route(t["x"], t["router_w"], k, cfg.norm_topk_prob, t["shared_gate"])
+    gr = moe.moe_align(ids, E, lay["block_m"])
+    act = moe.moe_gate_up(t["x"], t["w_gate_up"], gr, k)
+    y = moe.moe_down(act, t["w_down"], w, gr, N, k)
+    sy = None
+    if Is:
+        _, sy = moe.moe_shared_expert(t["x"], t["shared_w_gate_up"], t["shared_w_down"], sc)
+    ref = moe.moe_combine(y, N, k, sy)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
