@@ -177,3 +177,16 @@ def test_ids_products_reject_before_any_hip_call():
     assert lib.moe_down_ids(ctypes.byref(ok_p), fake, fake, fake, None, fake, None) == B.MOE_EINVAL
     p0 = moe.problem(0, 128, 16, 8, 64)
     assert lib.moe_gate_up_ids(ctypes.byref(p0), None, None, None, None, None) == 0
+
+
+def test_forward_schedule_choice():
+    """moe_forward takes the ids products for bf16 batches the grouped path
+    would run in 16-row tiles, with 4 <= N*k <= 1024, N*k % 4 == 0 and
+    N*k >= 1.5 E (most experts hit); otherwise the grouping."""
+    import torch
+    L = lambda *a, **kw: moe.moe_get_workspace_layout(moe.problem(*a, **kw))["ids_products"]
+    assert [L(N, 2048, 128, 8, 768) for N in (1, 16, 23, 24, 64, 128, 129, 4096)] == [0, 0, 0, 1, 1, 1, 0, 0]
+    assert L(64, 2048, 128, 8, 768, dtype=torch.float32) == 0
+    assert L(5, 128, 4, 3, 64) == 0                     # 15 pairs: not a multiple of 4
+    assert L(4, 128, 6, 2, 64) == 0                     # 8 pairs: 2 * 8 < 3 * 6
+    assert L(6, 128, 6, 2, 64) == 1                     # 12 pairs: 2 * 12 >= 3 * 6
