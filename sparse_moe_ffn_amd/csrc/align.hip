@@ -23,9 +23,11 @@
 // Atomics only count; every position comes from prefix sums, so the result
 // is the same on every run.
 //
-// One chunk (<= 4096 pairs): a single workgroup does everything.  More: three
-// launches (count per chunk, scan in one workgroup, scatter per chunk) with
-// the per-chunk counts in a caller-provided scratch array.
+// One chunk (<= 4096 pairs): a single workgroup does everything.  More: two
+// launches, with the per-chunk counts in a caller-provided scratch array:
+// count per chunk, then scan and scatter per chunk (every workgroup redoes
+// the small scan over the per-chunk counts, which saves a one-workgroup
+// launch between the two).
 #include "moe_common.h"
 #include "moe_launch.h"
 
@@ -95,7 +97,8 @@ __device__ __forceinline__ void scatter_range(const int32_t* ids, int beg, int e
 }
 
 // Wave 0: exclusive scans of cnt[] (rows) and of its tile counts over the
-// experts; writes seg_start, tile_start, offsets and num_tiles.
+// experts; writes seg_start, tile_start and (when not null) offsets and
+// num_tiles.
 __device__ __forceinline__ void scan_experts(const int* cnt, int E, int BM, int* seg_start, int* tile_start,
                                              int32_t* offsets, int32_t* num_tiles) {
   const int lane = lane_id();
@@ -114,12 +117,12 @@ __device__ __forceinline__ void scan_experts(const int* cnt, int E, int BM, int*
     if (e < E) {
       seg_start[e] = carry_rows + ic - c;
       tile_start[e] = carry_tiles + it - nt;
-      offsets[e] = carry_rows + ic - c;
+      if (offsets) offsets[e] = carry_rows + ic - c;
     }
     carry_rows += __shfl(ic, kWave - 1, kWave);
     carry_tiles += __shfl(it, kWave - 1, kWave);
   }
-  if (lane == 0) {
+  if (lane == 0 && offsets) {
     offsets[E] = carry_rows;
     num_tiles[0] = carry_tiles;
   }
@@ -215,65 +218,60 @@ __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(const int32_
   for (int i = threadIdx.x; i < E; i += kAlignThreads) chunk_counts[(int64_t)blockIdx.x * E + i] = h[i];
 }
 
-// chunk_counts -> per-chunk bases (in place), counts, offsets, tile starts
-// (scratch_tile_start[E]), tile table, padding, num_tiles.
-__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
-    int P, int E, int BM, int nchunks, int32_t* __restrict__ chunk_counts, int32_t* __restrict__ tile_start_out,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
-    int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_rows, int32_t* __restrict__ num_tiles) {
+// Scan and stable scatter of chunk blockIdx.x in one launch.  Every
+// workgroup reads all chunks' histograms (nchunks x E ints, a few KB) and
+// forms, in LDS, its chunk's base in every expert segment and the experts'
+// totals, segment starts and tile starts; workgroup 0 also writes counts,
+// offsets, num_tiles, the tile table and the sentinel padding.  The padding
+// rows of a segment lie past its pairs, so they never meet the scatter.
+__global__ __launch_bounds__(kAlignThreads) void align_scan_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int BM, int nchunks, const int32_t* __restrict__ chunk_counts,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ order,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ tile_expert, int32_t* __restrict__ tile_rows,
+    int32_t* __restrict__ num_tiles) {
+  __shared__ int hist[kAlignWaves][kMaxExperts];
   __shared__ int cnt[kMaxExperts];
+  __shared__ int base[kMaxExperts];
   __shared__ int seg_start[kMaxExperts];
   __shared__ int tile_start[kMaxExperts];
   __shared__ int total_tiles;
   const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int b = blockIdx.x;
+  const bool lead = b == 0;
+  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
   for (int e = tid; e < E; e += kAlignThreads) {
-    int run = 0;
+    int run = 0, mine = 0;
     for (int c0 = 0; c0 < nchunks; c0 += 8) {          // 8 independent loads in flight
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = (c0 + u < nchunks) ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (c0 + u < nchunks) chunk_counts[(int64_t)(c0 + u) * E + e] = run;
+        if (c0 + u == b) mine = run;                   // pairs of e in the chunks before this one
         run += v[u];
       }
     }
     cnt[e] = run;
-    counts[e] = run;
+    base[e] = mine;
+    if (lead) counts[e] = run;
   }
   __syncthreads();
-  if (tid < kWave) scan_experts(cnt, E, BM, seg_start, tile_start, offsets, num_tiles);
+  if (tid < kWave) scan_experts(cnt, E, BM, seg_start, tile_start, lead ? offsets : nullptr, num_tiles);
   __syncthreads();
-  for (int e = tid; e < E; e += kAlignThreads) tile_start_out[e] = tile_start[e];
-  if (tid == 0) total_tiles = tile_start[E - 1] + (cnt[E - 1] + BM - 1) / BM;
-  __syncthreads();
-  fill_tiles(cnt, tile_start, E, BM, P, total_tiles, sorted_pairs, tile_expert, tile_rows);
-}
-
-// Stable scatter of one chunk, starting from the chunk's bases.
-__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int BM, const int32_t* __restrict__ chunk_base,
-    const int32_t* __restrict__ tile_start_in, const int32_t* __restrict__ offsets, int32_t* __restrict__ order,
-    int32_t* __restrict__ sorted_pairs) {
-  __shared__ int hist[kAlignWaves][kMaxExperts];
-  __shared__ int seg_start[kMaxExperts];
-  __shared__ int tile_start[kMaxExperts];
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
-  for (int e = tid; e < E; e += kAlignThreads) {
-    seg_start[e] = offsets[e];
-    tile_start[e] = tile_start_in[e];
+  if (lead) {                                          // the whole workgroup takes this branch or none of it
+    if (tid == 0) total_tiles = tile_start[E - 1] + (cnt[E - 1] + BM - 1) / BM;
+    __syncthreads();
+    fill_tiles(cnt, tile_start, E, BM, P, total_tiles, sorted_pairs, tile_expert, tile_rows);
   }
-  __syncthreads();
-  const int c0 = blockIdx.x * kChunk;
+  const int c0 = b * kChunk;
   const int range = kChunk / kAlignWaves;
   const int beg = min(P, c0 + wave * range);
   const int end = min(P, beg + range);
   count_range(ids, beg, end, E, hist[wave]);
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) {
-    int run = chunk_base[(int64_t)blockIdx.x * E + e];
+    int run = base[e];
     for (int w = 0; w < kAlignWaves; ++w) {
       const int c = hist[w][e];
       hist[w][e] = run;
@@ -301,12 +299,9 @@ hipError_t launch_align(const int32_t* ids, int64_t num_pairs, int64_t num_exper
     return hipGetLastError();
   }
   int32_t* chunk_counts = scratch;
-  int32_t* tile_start = scratch + (int64_t)nchunks * E;
   hipLaunchKernelGGL(align_count_kernel, dim3(nchunks), dim3(kAlignThreads), 0, s, ids, P, E, chunk_counts);
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kAlignThreads), 0, s, P, E, BM, nchunks, chunk_counts,
-                     tile_start, counts, offsets, sorted_pairs, tile_expert, tile_rows, num_tiles);
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nchunks), dim3(kAlignThreads), 0, s, ids, P, E, BM, chunk_counts,
-                     tile_start, offsets, order, sorted_pairs);
+  hipLaunchKernelGGL(align_scan_scatter_kernel, dim3(nchunks), dim3(kAlignThreads), 0, s, ids, P, E, BM, nchunks,
+                     chunk_counts, counts, offsets, order, sorted_pairs, tile_expert, tile_rows, num_tiles);
   return hipGetLastError();
 }
 
