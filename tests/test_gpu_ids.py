@@ -120,3 +120,37 @@ def test_out_of_range_ids_match_no_expert():
     assert torch.equal(act_i[kd].view(torch.int16), act_g[rows_of_pair[keep].to(DEV)].view(torch.int16))
     assert torch.equal(y_i[kd].view(torch.int16), y_g[kd].view(torch.int16))
     assert bool((act_i[~kd] == 7.0).all()) and bool((y_i[~kd] == 7.0).all())
+
+
+def test_ids_forward_with_shared_expert_in_a_graph():
+    """moe_forward on the ids path (with a shared expert) captured once and
+    replayed with new inputs copied in, eager runs in between: every replay
+    equals the eager result."""
+    cfg = random_case(32, 256, 16, 4, 128, I_shared=64, seed=49)
+    inputs = [make_inputs(random_case(32, 256, 16, 4, 128, I_shared=64, seed=s), DEV) for s in (49, 50, 51)]
+    t = {k: (v.clone() if v is not None else None) for k, v in inputs[0].items()}
+    p = moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], cfg.top_k, cfg.norm_topk_prob, t["shared_w_gate_up"])
+    assert moe.moe_get_workspace_layout(p)["ids_products"] == 1
+    ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(t["x"])
+
+    def fwd(o):
+        return moe.moe_forward(t["x"], t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                               t["shared_w_gate_up"], t["shared_w_down"], t["shared_gate"], out=o, workspace=ws)
+    fwd(out)                                            # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd(out)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        for name, v in inputs[rep % 3].items():
+            if v is not None:
+                t[name].copy_(v)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = fwd(torch.empty_like(out))
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {rep}"
+    del graph
