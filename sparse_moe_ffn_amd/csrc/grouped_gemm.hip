@@ -143,16 +143,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   uint16_t* const ring_a = smem;
   uint16_t* const ring_b = smem + SA * kAStage;
   // Down: output row (pair index) and routing weight of every tile row,
-  // loaded once at the start so the epilogue reads them from LDS.  Scan mode
-  // (16-row tiles only) keeps the current pass's pairs in ep_row (down's
-  // table holds the same pairs) and, during the scan, the per-wave match
-  // counts in ep_scale (filled only afterwards).
-  static_assert(!SCAN || (BM == 16 && NW <= BM), "scan mode runs 16-row passes");
+  // loaded once at the start so the epilogue reads them from LDS.
+  __shared__ int32_t ep_row[MODE == kDown ? BM : 1];
+  __shared__ float ep_scale[MODE == kDown ? BM : 1];
+  // Scan mode (16-row tiles only): the current pass's pairs, and the
+  // per-wave match counts of the scan.
+  static_assert(!SCAN || BM == 16, "scan mode runs 16-row passes");
   constexpr bool scan = SCAN;
-  __shared__ int32_t ep_row[(MODE == kDown || SCAN) ? BM : 1];
-  __shared__ float ep_scale[(MODE == kDown || SCAN) ? BM : 1];
-  int32_t* const scan_rows = ep_row;
-  int32_t* const scan_count = reinterpret_cast<int32_t*>(ep_scale);
+  __shared__ int32_t scan_rows[SCAN ? BM : 1];
+  __shared__ int32_t scan_count[SCAN ? NW : 1];
 
   const bool grouped = !SCAN && g.sorted_pairs != nullptr;
   const int half = BN / 2;
