@@ -266,6 +266,38 @@ def test_full_size_parity(name):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("N", [64, 1024, 4096])
+def test_larger_layer_shape(N):
+    """A larger layer of the same family (H=4096, E=128, top-8, I=1536:
+    twice the reduction length of both products and of the router).  64
+    tokens take the ids products, 1024 and 4096 the grouped tiles.  Routing
+    is compared on every token and the output on sampled tokens; only the
+    experts those tokens use are copied to the host."""
+    cfg = random_case(N, 4096, 128, 8, 1536, dtype="bf16", seed=31)
+    t = make_inputs(cfg, DEV)
+    out = run_forward(t, cfg)
+    ids_gpu, w_gpu, _ = moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    torch.cuda.synchronize()
+    h = {"x": host(t["x"]), "router_w": host(t["router_w"])}
+    (ids_ref, w_ref, probs, margin), keep = compare_routing(h, cfg, ids_gpu, w_gpu)
+    rng = np.random.default_rng(N)
+    rows = [int(r) for r in sorted(set([0, N - 1] + rng.choice(N, size=4, replace=False).tolist())) if keep[r]]
+    used = sorted({int(e) for r in rows for e in ids_ref[r]})
+    slot = {e: i for i, e in enumerate(used)}
+    sub_ids = np.zeros_like(ids_ref)
+    for r in rows:
+        sub_ids[r] = [slot[int(e)] for e in ids_ref[r]]
+    sel = torch.tensor(used, device=DEV)
+    wgu = host(t["w_gate_up"].index_select(0, sel))
+    wd = host(t["w_down"].index_select(0, sel))
+    ref, _ = O.moe_forward(h["x"], h["router_w"], wgu, wd, cfg.top_k, cfg.norm_topk_prob, rows=rows,
+                           routing=(sub_ids, w_ref, probs, margin))
+    err, tol = check_output(host(out)[rows], ref, cfg.dtype, cfg.name)
+    print(f"{cfg.name}: err {err:.3e} tol {tol:.3e} rows {len(rows)} experts {len(used)} "
+          f"excluded {int((~keep).sum())}")
+
+
+@pytest.mark.slow
 def test_batch_invariance_decode_layer():
     cfg, t = full_inputs("decode")
     full = run_forward(t, cfg)
