@@ -109,15 +109,16 @@ int moe_get_workspace_layout(const moe_problem* p, moe_workspace_layout* layout)
 
 /* Expert weights in the blocked layout.  The pages fix only the weight
  * shapes (M03 L1 细节: Wg, Wu [I, H], Wd [H, I]); the layout is this
- * library's.  Each group of 8 rows is stored as consecutive 1 KB blocks of
- * 8 rows x 64 columns, so one K stage of a grouped product reads whole
- * blocks instead of 128 bytes from each of 8 rows 2*cols bytes apart; the
- * products then run a few per cent faster and give bit for bit the same
- * results as with row-major weights.  Meant as a one-time step when the
- * weights are loaded.
+ * library's.  Each matrix is stored as cols/64 panels of 64 columns, one
+ * after the other, and each panel holds all rows, 64 elements per row.
+ * One K stage of a grouped product (64 columns of a run of weight rows)
+ * is then one contiguous piece of memory instead of 128 bytes from each
+ * row, 2*cols bytes apart.  The products run faster and give bit for bit
+ * the same results as with row-major weights.  Meant as a one-time step
+ * when the weights are loaded.
  *   src [batch, rows, cols] bf16 row-major; dst the same number of bf16
  *   elements, element (b, r, c) at
- *     b*rows*cols + ((r/8)*(cols/64) + c/64)*512 + (r%8)*64 + c%64.
+ *     b*rows*cols + (c/64)*rows*64 + r*64 + c%64.
  *   w_gate_up: batch E, rows 2I, cols H;  w_down: batch E, rows H, cols I;
  *   shared expert and dense layers: batch 1.
  * dtype must be MOE_BF16; rows % 8 == 0 and cols % 64 == 0; src and dst

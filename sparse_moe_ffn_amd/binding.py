@@ -140,7 +140,7 @@ def problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up
 def moe_pack_weights(w, out=None):
     """`w` ([rows, cols] or [batch, rows, cols], bf16, row-major) in the
     blocked layout of moe_pack_weights: a tensor of the same shape whose
-    storage holds the blocks (index it only through the library)."""
+    storage holds the 64-column panels (index it only through the library)."""
     w = _gpu(w, "w", torch.bfloat16)
     if w.dim() not in (2, 3):
         raise ValueError("w must be [rows, cols] or [batch, rows, cols]")

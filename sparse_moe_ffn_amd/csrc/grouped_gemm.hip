@@ -226,11 +226,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
                         : min((int64_t)g.n_out + nt * half + (j - half), b_rows - 1);
     else
       wrow = min((int64_t)nt * BN + j, b_rows - 1);
-    // Row-major: row wrow starts at wrow * K.  Blocked: the 8-row group of
-    // wrow starts at (wrow / 8) * 8K, its 64-column blocks follow one
-    // another (512 elements each), and row wrow % 8 sits 64 * (wrow % 8)
-    // into each block; issue_b scales the K offset by 8 to match.
-    src_b[q] = (BLK ? B + (wrow >> 3) * ((int64_t)K * 8) + (wrow & 7) * 64 : B + wrow * K) + chunk * 8;
+    // Row-major: row wrow starts at wrow * K.  Blocked: each 64-column
+    // panel holds all b_rows rows, 64 elements each, so row wrow starts at
+    // wrow * 64 in every panel; issue_b adds the panel offset (stage start
+    // times b_rows).
+    src_b[q] = (BLK ? B + wrow * 64 : B + wrow * K) + chunk * 8;
   }
 
   const int nk = K / BK;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
                                 : (!scan && m_tiles > 1);
   auto issue_b = [&](int kt) {
     const uint32_t base = lds_addr(ring_b + (kt % SB) * kBStage);
-    const int ko = BLK ? kpos(kt) * 8 : kpos(kt);
+    const int64_t ko = BLK ? kpos(kt) * b_rows : kpos(kt);
     if (shared_b) {
 #pragma unroll
       for (int q = 0; q < B_PER_WAVE; ++q)
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(kF32Threads) void grouped_gemm_f32_kernel(GemmProbl
 
 // ---------------------------------------------------------------- weight packing
 // dst (blocked) from src (row-major [batch, rows, cols]): each thread moves one
-// 16-byte piece (8 elements of one row inside one 64-column block).
+// 16-byte piece (8 elements of one row inside one 64-column panel).
 __global__ __launch_bounds__(256) void pack_weights_bf16_kernel(const uint16_t* __restrict__ src,
                                                                 uint16_t* __restrict__ dst, int64_t pieces,
                                                                 int64_t rows, int64_t cols) {
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(256) void pack_weights_bf16_kernel(const uint16_t* 
   const int64_t r_all = i / per_row;                 // batch * rows + row
   const int64_t c = (i % per_row) * 8;               // first column of the piece
   const int64_t b = r_all / rows, r = r_all % rows;
-  const int64_t d = b * rows * cols + ((r >> 3) * (cols / 64) + (c >> 6)) * 512 + (r & 7) * 64 + (c & 63);
+  const int64_t d = b * rows * cols + (c >> 6) * (rows * 64) + r * 64 + (c & 63);
   *reinterpret_cast<uint4*>(dst + d) = *reinterpret_cast<const uint4*>(src + r_all * cols + c);
 }
 
@@ -622,7 +622,11 @@ hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_
 // ---------------------------------------------------------------- launchers
 
 // ROT: K-start stride.  Both weight layouts use the same stride, so they
-// sum in the same order and give bit for bit the same results.
+// sum in the same order and give bit for bit the same results.  Measured
+// with blocked weights: 16-row tiles at 64 tokens, gate/up 116.6 -> 115.2 us
+// and down 60.7 -> 59.9 us from stride 5 to 13 (row-major 116.6 -> 117.3
+// and 63.1 -> 62.2 us); 320-row tiles at 4096 tokens, gate/up 214.6 ->
+// 210.8 us from stride 1 to 5.
 // SCAN: the small-batch products that scan the top-k ids (16-row tiles).
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = 7, bool SCAN = false>
 static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
@@ -665,19 +669,19 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     //     expert with a second pass ends the last of exactly two rounds late.
     // Results are the same bit for bit: the tile width does not change any
     // row's arithmetic.
-    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, 5, true>(g, s);
-    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 8, 2, 2, MODE, 5, true>(g, s);
-    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 5, true>(g, s);
+    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, 13, true>(g, s);
+    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 8, 2, 2, MODE, 13, true>(g, s);
+    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 13, true>(g, s);
   }
   switch (g.block_m) {
-    case 16:   // decode.  K-start stride 5: gate/up at 64 tokens 130 -> 127 us with blocked
-               // weights, unchanged row-major; down one weight slot shorter (75 -> 74 us)
-      if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE, 5>(g, s);
-      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 5>(g, s);
+    case 16:   // small batches; K-start stride 13 like the scan-mode products, whose rows
+               // must match these tiles bit for bit; down one weight slot shorter (75 -> 74 us)
+      if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE, 13>(g, s);
+      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 13>(g, s);
     case 32: return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, s);
     case 64: return launch_bf16<64, 256, 64, 1, 4, 2, 3, MODE>(g, s);
     case 128: return launch_bf16<128, 256, 64, 2, 4, 2, 3, MODE>(g, s);
-    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE, 1>(g, s);   // stride 1: blocked gate/up 216 -> 208 us
+    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE, 5>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -28,8 +28,8 @@ def test_pack_follows_index_formula(shape):
     packed = moe.moe_pack_weights(w)
     torch.cuda.synchronize()
     b, r, c = (1,) + shape if len(shape) == 2 else shape
-    # element (b, r, c) at b*R*C + ((r/8)*(C/64) + c/64)*512 + (r%8)*64 + c%64
-    expect = bits.reshape(b, r // 8, 8, c // 64, 64).permute(0, 1, 3, 2, 4).reshape(-1)
+    # element (b, r, c) at b*R*C + (c/64)*R*64 + r*64 + c%64: 64-column panels, rows inside
+    expect = bits.reshape(b, r, c // 64, 64).permute(0, 2, 1, 3).reshape(-1)
     assert torch.equal(packed.cpu().view(torch.int16).reshape(-1), expect)
 
 
