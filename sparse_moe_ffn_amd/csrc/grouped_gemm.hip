@@ -667,10 +667,13 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     //     59.2 / 62.3 / 64.5: better while experts average at most 4 pairs
     //     (then nearly all take one 16-row pass), worse at 8, where the odd
     //     expert with a second pass ends the last of exactly two rounds late.
+    //     With 4 waves (two workgroups per CU) and the panel weight layout,
+    //     50.2 / 54.1 / 59.2 us at 24 / 32 / 64 tokens against 51.6 / 54.8 /
+    //     60.0 with 8 waves.
     // Results are the same bit for bit: the tile width does not change any
     // row's arithmetic.
     if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, 13, true>(g, s);
-    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 8, 2, 2, MODE, 13, true>(g, s);
+    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, 13, true>(g, s);
     else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 13, true>(g, s);
   }
   switch (g.block_m) {
