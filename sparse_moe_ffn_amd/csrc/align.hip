@@ -13,7 +13,7 @@
 //   scan:      per-expert exclusive prefixes over the ranges (each range's
 //              base inside its expert), then over the experts for the
 //              unpadded segment starts, the tile starts and the padded rows;
-//   scatter:   each wave walks its range 64 pairs at a time; lanes holding
+//   scatter:   each wave takes its range 64 pairs at a time; lanes holding
 //              the same expert find each other with one ballot per id bit, a
 //              lane's rank is the number of matching lanes below it, and the
 //              highest matching lane advances the running position.  Ranges
@@ -37,6 +37,7 @@ constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kAlignUnroll = 4;
 constexpr int kChunk = kAlignWaves * kWave * kAlignUnroll;     // pairs per chunk (4096)
+static_assert(kChunk / kAlignWaves == kWave * kAlignUnroll, "a wave range is one load of kAlignUnroll ids per lane");
 
 // Expert id of pair p, or -1 past the end / outside [0, E) (dropped).
 __device__ __forceinline__ int pair_expert(const int32_t* ids, int p, int end, int E) {
@@ -56,42 +57,42 @@ __device__ __forceinline__ unsigned long long match_lanes(int e, int nbits) {
   return match;
 }
 
-// Histogram of pairs [beg, end) into h[e] (LDS atomics, counts only).
-__device__ __forceinline__ void count_range(const int32_t* ids, int beg, int end, int E, int* h) {
+// A wave range holds at most kWave * kAlignUnroll pairs, kAlignUnroll per
+// lane: its ids are loaded once, first thing, so that the load overlaps the
+// kernel's other start-up reads, and serve both the histogram and the
+// scatter.  e[u] is the expert of pair beg + u * kWave + lane, or -1.
+__device__ __forceinline__ void load_range(const int32_t* ids, int beg, int end, int E, int (&e)[kAlignUnroll]) {
   const int lane = lane_id();
-  for (int p0 = beg; p0 < end; p0 += kWave * kAlignUnroll) {
-    int e[kAlignUnroll];
 #pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u) e[u] = pair_expert(ids, p0 + u * kWave + lane, end, E);
-#pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u)
-      if (e[u] >= 0) atomicAdd(&h[e[u]], 1);
-  }
+  for (int u = 0; u < kAlignUnroll; ++u) e[u] = pair_expert(ids, beg + u * kWave + lane, end, E);
 }
 
-// Stable scatter of pairs [beg, end): pos[e] holds the running position of
-// expert e inside its segment for this range (advanced in place).
-__device__ __forceinline__ void scatter_range(const int32_t* ids, int beg, int end, int E, int BM, int nbits,
-                                              int* pos, const int* seg_start, const int* tile_start,
-                                              int32_t* order, int32_t* sorted_pairs) {
+// Histogram of a wave range into h[e] (LDS atomics, counts only).
+__device__ __forceinline__ void count_range(const int (&e)[kAlignUnroll], int* h) {
+#pragma unroll
+  for (int u = 0; u < kAlignUnroll; ++u)
+    if (e[u] >= 0) atomicAdd(&h[e[u]], 1);
+}
+
+// Stable scatter of a wave range starting at pair beg: pos[e] holds the
+// running position of expert e inside its segment for this range (advanced
+// in place).
+__device__ __forceinline__ void scatter_range(const int (&ev)[kAlignUnroll], int beg, int BM, int nbits, int* pos,
+                                              const int* seg_start, const int* tile_start, int32_t* order,
+                                              int32_t* sorted_pairs) {
   const int lane = lane_id();
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int p0 = beg; p0 < end; p0 += kWave * kAlignUnroll) {
-    int ev[kAlignUnroll];
 #pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u) ev[u] = pair_expert(ids, p0 + u * kWave + lane, end, E);
-#pragma unroll
-    for (int u = 0; u < kAlignUnroll; ++u) {
-      const int p = p0 + u * kWave + lane;
-      const int e = ev[u];
-      const unsigned long long match = match_lanes(e, nbits);
-      if (e >= 0) {
-        const int rank = __popcll(match & below);
-        const int at = pos[e] + rank;
-        order[seg_start[e] + at] = p;
-        sorted_pairs[tile_start[e] * BM + at] = p;
-        if ((match >> lane) == 1ull) pos[e] = at + 1;          // highest matching lane
-      }
+  for (int u = 0; u < kAlignUnroll; ++u) {
+    const int p = beg + u * kWave + lane;
+    const int e = ev[u];
+    const unsigned long long match = match_lanes(e, nbits);
+    if (e >= 0) {
+      const int rank = __popcll(match & below);
+      const int at = pos[e] + rank;
+      order[seg_start[e] + at] = p;
+      sorted_pairs[tile_start[e] * BM + at] = p;
+      if ((match >> lane) == 1ull) pos[e] = at + 1;          // highest matching lane
     }
   }
 }
@@ -174,13 +175,16 @@ __global__ __launch_bounds__(kAlignThreads) void align_single_kernel(
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int nbits = nbits_of(E);
-
-  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
-  __syncthreads();
+  // P <= kChunk, so a wave range is at most kWave * kAlignUnroll pairs.
   const int range = ((P + kAlignWaves * kWave - 1) / (kAlignWaves * kWave)) * kWave;
   const int beg = min(P, wave * range);
   const int end = min(P, beg + range);
-  count_range(ids, beg, end, E, hist[wave]);
+  int ev[kAlignUnroll];
+  load_range(ids, beg, end, E, ev);
+
+  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  count_range(ev, hist[wave]);
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) {
     int run = 0;
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_single_kernel(
   __syncthreads();
   if (wave == 0) scan_experts(cnt, E, BM, seg_start, tile_start, offsets, num_tiles);
   __syncthreads();
-  scatter_range(ids, beg, end, E, BM, nbits, hist[wave], seg_start, tile_start, order, sorted_pairs);
+  scatter_range(ev, beg, BM, nbits, hist[wave], seg_start, tile_start, order, sorted_pairs);
   const int total = tile_start[E - 1] + (cnt[E - 1] + BM - 1) / BM;
   fill_tiles(cnt, tile_start, E, BM, P, total, sorted_pairs, tile_expert, tile_rows);
 }
@@ -206,14 +210,16 @@ __global__ __launch_bounds__(kAlignThreads) void align_single_kernel(
 __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(const int32_t* __restrict__ ids, int P,
                                                                      int E, int32_t* __restrict__ chunk_counts) {
   __shared__ int h[kMaxExperts];
-  for (int i = threadIdx.x; i < E; i += kAlignThreads) h[i] = 0;
-  __syncthreads();
   const int c0 = blockIdx.x * kChunk;
   const int wave = threadIdx.x / kWave;
   const int range = kChunk / kAlignWaves;
   const int beg = min(P, c0 + wave * range);
   const int end = min(P, beg + range);
-  count_range(ids, beg, end, E, h);
+  int ev[kAlignUnroll];
+  load_range(ids, beg, end, E, ev);
+  for (int i = threadIdx.x; i < E; i += kAlignThreads) h[i] = 0;
+  __syncthreads();
+  count_range(ev, h);
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += kAlignThreads) chunk_counts[(int64_t)blockIdx.x * E + i] = h[i];
 }
@@ -239,6 +245,11 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_scatter_kernel(
   const int wave = tid / kWave;
   const int b = blockIdx.x;
   const bool lead = b == 0;
+  const int range = kChunk / kAlignWaves;
+  const int beg = min(P, b * kChunk + wave * range);
+  const int end = min(P, beg + range);
+  int ev[kAlignUnroll];
+  load_range(ids, beg, end, E, ev);                    // in flight with the chunk counts below
   for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
   for (int e = tid; e < E; e += kAlignThreads) {
     int run = 0, mine = 0;
@@ -264,11 +275,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_scatter_kernel(
     __syncthreads();
     fill_tiles(cnt, tile_start, E, BM, P, total_tiles, sorted_pairs, tile_expert, tile_rows);
   }
-  const int c0 = b * kChunk;
-  const int range = kChunk / kAlignWaves;
-  const int beg = min(P, c0 + wave * range);
-  const int end = min(P, beg + range);
-  count_range(ids, beg, end, E, hist[wave]);
+  count_range(ev, hist[wave]);
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) {
     int run = base[e];
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_scatter_kernel(
     }
   }
   __syncthreads();
-  scatter_range(ids, beg, end, E, BM, nbits_of(E), hist[wave], seg_start, tile_start, order, sorted_pairs);
+  scatter_range(ev, beg, BM, nbits_of(E), hist[wave], seg_start, tile_start, order, sorted_pairs);
 }
 
 int64_t align_scratch_ints(int64_t num_pairs, int64_t num_experts) {
