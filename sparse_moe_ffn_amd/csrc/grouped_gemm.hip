@@ -110,6 +110,8 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 
+constexpr int kRot = 13;   // K-start stride of every grouped product (see the launchers)
+
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK, int ROT, bool SCAN>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
   static_assert(BK == 32 || BK == 64, "stage depth");
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // the same low address bits, and so on the same few HBM channels, if all
   // workgroups walk K in step; rotating the start by expert spreads them,
   // while the column blocks of one expert stay in step and keep sharing its
-  // A rows in L2.  The stride ROT is tuned per tile shape (measured).  The
+  // A rows in L2.  The stride is the same for every tile shape and the
   // start depends only on the expert, so every output element keeps one
   // summation order whatever the batch.
   const int kstart = (expert * ROT) % nk;
@@ -621,14 +623,16 @@ hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_
 
 // ---------------------------------------------------------------- launchers
 
-// ROT: K-start stride.  Both weight layouts use the same stride, so they
-// sum in the same order and give bit for bit the same results.  Measured
-// with blocked weights: 16-row tiles at 64 tokens, gate/up 116.6 -> 115.2 us
-// and down 60.7 -> 59.9 us from stride 5 to 13 (row-major 116.6 -> 117.3
-// and 63.1 -> 62.2 us); 320-row tiles at 4096 tokens, gate/up 214.6 ->
-// 210.8 us from stride 1 to 5.
+// ROT: K-start stride, kRot for every tile shape and both weight layouts,
+// so every output element is summed in one order whatever the tile height:
+// a token's output does not depend on the batch it comes in, nor on the
+// weight layout.  Measured with blocked weights: 16-row tiles at 64 tokens,
+// gate/up 116.6 -> 115.2 us and down 60.7 -> 59.9 us from stride 5 to 13
+// (row-major 116.6 -> 117.3 and 63.1 -> 62.2 us); moe_forward with the
+// 32-, 64-, 128- and 320-row tiles (512 to 16384 tokens) within 1.2 us of
+// strides 7 and 5.
 // SCAN: the small-batch products that scan the top-k ids (16-row tiles).
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = 7, bool SCAN = false>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = kRot, bool SCAN = false>
 static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
   if (g.block_m != BM) return hipErrorInvalidValue;   // tiles must be laid out for this height
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
@@ -672,19 +676,18 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     //     60.0 with 8 waves.
     // Results are the same bit for bit: the tile width does not change any
     // row's arithmetic.
-    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, 13, true>(g, s);
-    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, 13, true>(g, s);
-    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 13, true>(g, s);
+    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, kRot, true>(g, s);
+    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, kRot, true>(g, s);
+    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, kRot, true>(g, s);
   }
   switch (g.block_m) {
-    case 16:   // small batches; K-start stride 13 like the scan-mode products, whose rows
-               // must match these tiles bit for bit; down one weight slot shorter (75 -> 74 us)
-      if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE, 13>(g, s);
-      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, 13>(g, s);
+    case 16:   // small batches; down one weight slot shorter (75 -> 74 us)
+      if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, s);
+      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE>(g, s);
     case 32: return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, s);
     case 64: return launch_bf16<64, 256, 64, 1, 4, 2, 3, MODE>(g, s);
     case 128: return launch_bf16<128, 256, 64, 2, 4, 2, 3, MODE>(g, s);
-    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE, 5>(g, s);
+    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE>(g, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -308,6 +308,25 @@ def test_batch_invariance_decode_layer():
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("name,sizes", [("prefill", [1, 64, 600, 1024, 2048]), ("talker", [1, 24, 600, 4096])])
+def test_batch_invariance_across_tile_heights(name, sizes):
+    """A token's output is the same bit for bit in any batch.  The first n
+    tokens of the layer run, by batch size, 16-row tiles (1 token), the ids
+    products (24 or 64), 32-, 64- and 128-row tiles (600, 1024, 2048) and
+    320-row tiles (4096 and the whole batch); with the shared expert its
+    dense products change tile height too.  Routing sums fixed H slices and
+    every product sums each output element in one K order whatever its tile,
+    so the rows must agree exactly."""
+    cfg, t = full_inputs(name)
+    full = run_forward(t, cfg)
+    for n in sizes:
+        sub = moe.moe_forward(t["x"][:n].contiguous(), t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k,
+                              cfg.norm_topk_prob, t["shared_w_gate_up"], t["shared_w_down"], t["shared_gate"])
+        torch.cuda.synchronize()
+        assert torch.equal(sub, full[:n]), f"{name}: the first {n} tokens differ from the whole batch"
+
+
+@pytest.mark.slow
 def test_staged_calls_equal_forward():
     cfg, t = full_inputs("decode")
     out = run_forward(t, cfg)
