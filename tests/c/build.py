@@ -11,8 +11,12 @@ EXE = os.path.join(HERE, "forward_gpu")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
+def c_compiler():
+    return shutil.which("gcc") or shutil.which("cc")
+
+
 def build() -> str:
-    cc = shutil.which("gcc") or shutil.which("cc")
+    cc = c_compiler()
     if cc is None:
         raise RuntimeError("no C compiler")
     cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
