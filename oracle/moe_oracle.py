@@ -15,7 +15,7 @@ Sources (the pages this follows, by title and section):
 * [NANO] the nano-vLLM Qwen3-30B-A3B notes at lshu.cn/news/442807,
   qwen3_moe.py, class ``Qwen3MoeSparseMoeBlock``
   (router linear, float32 softmax, top-k, renormalisation, cast of the
-  routing weights to the input dtype, one-hot expert mask, index_add_).
+  routing weights to the input dtype, scaled expert outputs added per token).
 * [Q35] "Qwen3.5 推理全流程", section 2.5B "Sparse MoE" (shared expert gated
   by a sigmoid of a per-token scalar) and 2.5A "Dense MLP".
 * [STEP19] "Step 19: Real Model — Qwen3ForCausalLM", section "RMSNorm：去掉
@@ -254,15 +254,18 @@ def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, shared=No
     return out, routing
 
 
-def moe_forward_grouped(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, shared=None):
+def moe_forward_grouped(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, shared=None, routing=None):
     """The "serving way" of [M03] 题面速览 and L2: group the pairs by expert,
     run each non-empty expert once over its gathered tokens, scale by the
     routing weights and index-add back to the tokens.  A second formulation,
-    used to cross-check ``moe_forward``."""
+    used to cross-check ``moe_forward``; ``routing`` may pass a precomputed
+    ``route`` result."""
     x = np.asarray(x, dtype=F64)
     N, H = x.shape
     E = np.asarray(router_w).shape[0]
-    ids, w, probs, margin = route(x, router_w, top_k, norm_topk_prob)
+    if routing is None:
+        routing = route(x, router_w, top_k, norm_topk_prob)
+    ids, w, probs, margin = routing
     flat_e, flat_w, flat_tok = flatten_pairs(ids, w)
     order, counts, offsets = group_pairs(flat_e, E)
     experts = _ExpertCache(w_gate_up, w_down)
@@ -284,25 +287,23 @@ def moe_forward_grouped(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, s
     return out, (ids, w, probs, margin), (order, counts, offsets)
 
 
-def moe_forward_masked(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, shared=None):
-    """A third formulation ([NANO] Qwen3MoeSparseMoeBlock.forward): a one-hot
-    expert mask [E, k, N]; for every hit expert, the (slot, token) positions
-    where it is selected; each contribution is index-added."""
+def moe_forward_by_slot(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, shared=None):
+    """A third formulation, slot by slot: the block formula's sum over the k
+    routed experts of a token ([M03] 题面速览) taken with the slot index
+    outermost.  For slot j, the tokens whose j-th choice is expert e form one
+    batch through that expert; each token occurs once per slot, so the batch
+    rows are distinct and are added to their tokens directly."""
     x = np.asarray(x, dtype=F64)
     N, H = x.shape
-    E = np.asarray(router_w).shape[0]
     ids, w, _, _ = route(x, router_w, top_k, norm_topk_prob)
-    mask = np.zeros((E, top_k, N), dtype=bool)
-    for n in range(N):
-        for j in range(top_k):
-            mask[ids[n, j], j, n] = True
     experts = _ExpertCache(w_gate_up, w_down)
     out = np.zeros((N, H), dtype=F64)
-    for e in np.nonzero(mask.sum(axis=(1, 2)) > 0)[0]:
-        slot, tok = np.nonzero(mask[e])
-        wg, wu, wd = experts[int(e)]
-        y = swiglu(x[tok], wg, wu, wd) * w[tok, slot].astype(F64)[:, None]
-        np.add.at(out, tok, y)
+    for j in range(top_k):
+        col = ids[:, j]
+        for e in sorted(set(int(v) for v in col)):
+            rows = np.flatnonzero(col == e)
+            wg, wu, wd = experts[e]
+            out[rows] += w[rows, j].astype(F64)[:, None] * swiglu(x[rows], wg, wu, wd)
     if shared is not None:
         for n in range(N):
             out[n] += shared_term(x[n], shared)

@@ -119,6 +119,45 @@ def _gpu(t: torch.Tensor, name: str, dtype=None, device=None) -> torch.Tensor:
     return t
 
 
+def _tensor(t, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    return t
+
+
+def _shape(t, name: str, shape) -> torch.Tensor:
+    """Raise ValueError unless `t` has exactly `shape`.  Every binding checks
+    the shape of each tensor it passes, before any device check or launch: a
+    mis-shaped tensor would size the kernels' reads and writes wrongly."""
+    _tensor(t, name)
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(d) for d in shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _rank(t, name: str, ndim: int) -> torch.Tensor:
+    _tensor(t, name)
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return t
+
+
+def _numel_at_least(t, name: str, n: int) -> torch.Tensor:
+    _tensor(t, name)
+    if t.numel() < n:
+        raise ValueError(f"{name} must hold at least {n} elements, got {t.numel()}")
+    return t
+
+
+def _rows_cols(t, name: str, min_rows: int, cols: int) -> torch.Tensor:
+    """A 2-D tensor with exactly `cols` columns and at least `min_rows` rows
+    (intermediate buffers may be larger than one call needs)."""
+    _rank(t, name, 2)
+    if t.shape[1] != cols or t.shape[0] < min_rows:
+        raise ValueError(f"{name} must have shape (>= {min_rows}, {cols}), got {tuple(t.shape)}")
+    return t
+
+
 def problem(num_tokens, hidden, num_experts, top_k, inter, shared_inter=0, dtype=torch.bfloat16,
             norm_topk_prob=True, weight_layout=MOE_LAYOUT_ROW_MAJOR) -> MoEProblem:
     if dtype not in _DTYPES:
@@ -129,10 +168,15 @@ def problem(num_tokens, hidden, num_experts, top_k, inter, shared_inter=0, dtype
 
 def problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up=None,
                  weight_layout=MOE_LAYOUT_ROW_MAJOR) -> MoEProblem:
-    N, H = x.shape
-    E, two_i, H2 = w_gate_up.shape
-    if H2 != H or two_i % 2 or router_w.shape != (E, H):
-        raise ValueError("shape mismatch between x, router_w and w_gate_up")
+    N, H = _rank(x, "x", 2).shape
+    E, two_i, H2 = _rank(w_gate_up, "w_gate_up", 3).shape
+    if H2 != H or two_i % 2:
+        raise ValueError(f"w_gate_up must have shape (E, 2I, {H}), got {tuple(w_gate_up.shape)}")
+    _shape(router_w, "router_w", (E, H))
+    if shared_w_gate_up is not None:
+        Is2, H3 = _rank(shared_w_gate_up, "shared_w_gate_up", 2).shape
+        if H3 != H or Is2 % 2:
+            raise ValueError(f"shared_w_gate_up must have shape (2I_s, {H}), got {tuple(shared_w_gate_up.shape)}")
     Is = 0 if shared_w_gate_up is None else shared_w_gate_up.shape[0] // 2
     return problem(N, H, E, top_k, two_i // 2, Is, x.dtype, norm_topk_prob, weight_layout)
 
@@ -182,16 +226,23 @@ def moe_route_scratch_size(p: MoEProblem) -> int:
 def moe_route(x, router_w, top_k, norm_topk_prob, shared_gate=None, topk_ids=None, topk_w=None,
               shared_scale=None, scratch=None):
     """(topk_ids int32 [N,k], topk_w float32 [N,k], shared_scale float32 [N] or None)."""
+    N, H = _rank(x, "x", 2).shape
+    E = _rank(router_w, "router_w", 2).shape[0]
+    _shape(router_w, "router_w", (E, H))
+    if shared_gate is not None and _tensor(shared_gate, "shared_gate").numel() != H:
+        raise ValueError(f"shared_gate must have {H} elements, got {shared_gate.numel()}")
+    for t, n, shape in ((topk_ids, "topk_ids", (N, top_k)), (topk_w, "topk_w", (N, top_k)),
+                        (shared_scale, "shared_scale", (N,))):
+        if t is not None:
+            _shape(t, n, shape)
+    p = problem(N, H, E, top_k, 1, 0, x.dtype, norm_topk_prob)
+    if scratch is not None:
+        _numel_at_least(scratch, "scratch", -(-moe_route_scratch_size(p) // 4))
     x = _gpu(x, "x")
     dev = x.device
     router_w = _gpu(router_w, "router_w", x.dtype, dev)
-    N, H = x.shape
-    E = router_w.shape[0]
-    p = problem(N, H, E, top_k, 1, 0, x.dtype, norm_topk_prob)
     if shared_gate is not None:
         shared_gate = _gpu(shared_gate, "shared_gate", x.dtype, dev)
-        if shared_gate.numel() != H:
-            raise ValueError("shared_gate must have H elements")
         if shared_scale is None:
             shared_scale = torch.empty(N, dtype=torch.float32, device=dev)
     if topk_ids is None:
@@ -200,6 +251,11 @@ def moe_route(x, router_w, top_k, norm_topk_prob, shared_gate=None, topk_ids=Non
         topk_w = torch.empty((N, top_k), dtype=torch.float32, device=dev)
     if scratch is None:
         scratch = torch.empty(max(1, moe_route_scratch_size(p) // 4), dtype=torch.float32, device=dev)
+    _gpu(topk_ids, "topk_ids", torch.int32, dev)
+    _gpu(topk_w, "topk_w", torch.float32, dev)
+    if shared_scale is not None:
+        _gpu(shared_scale, "shared_scale", torch.float32, dev)
+    _gpu(scratch, "scratch", torch.float32, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_route(ctypes.byref(p), _ptr(x), _ptr(router_w), _ptr(shared_gate),
                                         _ptr(topk_ids), _ptr(topk_w), _ptr(shared_scale), _ptr(scratch),
@@ -219,6 +275,8 @@ class Grouping:
     block_m: int
     max_rows: int
     max_tiles: int
+    num_experts: int
+    num_pairs: int
 
 
 def moe_align_scratch_size(num_pairs: int, num_experts: int) -> int:
@@ -228,18 +286,22 @@ def moe_align_scratch_size(num_pairs: int, num_experts: int) -> int:
 
 
 def moe_align(topk_ids, num_experts: int, block_m: int, scratch=None) -> Grouping:
-    topk_ids = _gpu(topk_ids, "topk_ids", torch.int32)
-    dev = topk_ids.device
-    N, k = topk_ids.shape
+    N, k = _rank(topk_ids, "topk_ids", 2).shape
     P = N * k
     max_rows, max_tiles = moe_align_capacity(P, num_experts, block_m)
+    need = moe_align_scratch_size(P, num_experts)
+    if need and scratch is not None:
+        _numel_at_least(scratch, "scratch", need // 4)
+    topk_ids = _gpu(topk_ids, "topk_ids", torch.int32)
+    dev = topk_ids.device
     i32 = dict(dtype=torch.int32, device=dev)
     g = Grouping(torch.empty(num_experts, **i32), torch.empty(num_experts + 1, **i32), torch.empty(P, **i32),
                  torch.empty(max_rows, **i32), torch.empty(max_tiles, **i32), torch.empty(max_tiles, **i32),
-                 torch.empty(1, **i32), block_m, max_rows, max_tiles)
-    need = moe_align_scratch_size(P, num_experts)
+                 torch.empty(1, **i32), block_m, max_rows, max_tiles, num_experts, P)
     if scratch is None and need:
         scratch = torch.empty(need // 4, **i32)
+    if need:
+        _gpu(scratch, "scratch", torch.int32, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_align(_ptr(topk_ids), N, k, num_experts, block_m, _ptr(g.counts),
                                         _ptr(g.offsets), _ptr(g.order), _ptr(g.sorted_pairs),
@@ -248,16 +310,37 @@ def moe_align(topk_ids, num_experts: int, block_m: int, scratch=None) -> Groupin
     return g
 
 
+def _check_grouping(grouping: Grouping, num_pairs: int, num_experts: int):
+    """The grouping must be the one moe_align made for these pairs and experts:
+    its tile table sizes the products' grids and its pair indices address
+    their rows."""
+    if grouping.num_pairs != num_pairs or grouping.num_experts != num_experts:
+        raise ValueError(f"grouping was made for {grouping.num_pairs} pairs and {grouping.num_experts} experts, "
+                         f"not {num_pairs} and {num_experts}")
+    rows, tiles = moe_align_capacity(num_pairs, num_experts, grouping.block_m)
+    if (grouping.max_rows, grouping.max_tiles) != (rows, tiles):
+        raise ValueError("grouping capacity does not match its pairs, experts and block_m")
+    for t, n, shape in ((grouping.sorted_pairs, "sorted_pairs", (rows,)), (grouping.tile_expert, "tile_expert", (tiles,)),
+                        (grouping.tile_rows, "tile_rows", (tiles,)), (grouping.num_tiles, "num_tiles", (1,))):
+        _shape(t, "grouping." + n, shape)
+
+
 def moe_gate_up(x, w_gate_up, grouping: Grouping, top_k: int, act=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """act [max_rows, I] in x.dtype (rows of sentinel pairs are not written)."""
+    N, H = _rank(x, "x", 2).shape
+    E, two_i, H2 = _rank(w_gate_up, "w_gate_up", 3).shape
+    if H2 != H or two_i % 2:
+        raise ValueError(f"w_gate_up must have shape (E, 2I, {H}), got {tuple(w_gate_up.shape)}")
+    _check_grouping(grouping, N * top_k, E)
+    if act is not None:
+        _rows_cols(act, "act", grouping.max_rows, two_i // 2)
     x = _gpu(x, "x")
     dev = x.device
     w_gate_up = _gpu(w_gate_up, "w_gate_up", x.dtype, dev)
-    N, H = x.shape
-    E, two_i, _ = w_gate_up.shape
     p = problem(N, H, E, top_k, two_i // 2, 0, x.dtype, weight_layout=weight_layout)
     if act is None:
         act = torch.empty((grouping.max_rows, two_i // 2), dtype=x.dtype, device=dev)
+    _gpu(act, "act", x.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_gate_up(ctypes.byref(p), _ptr(x), _ptr(w_gate_up), _ptr(grouping.sorted_pairs),
                                           _ptr(grouping.tile_expert), _ptr(grouping.tile_rows),
@@ -269,14 +352,21 @@ def moe_gate_up(x, w_gate_up, grouping: Grouping, top_k: int, act=None, weight_l
 def moe_down(act, w_down, topk_w, grouping: Grouping, num_tokens: int, top_k: int, y=None,
              weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """y [N*k, H] in act.dtype: y[p] = topk_w[p] * (act[row of p] . w_down[e]^T)."""
+    E, H, I = _rank(w_down, "w_down", 3).shape
+    _check_grouping(grouping, num_tokens * top_k, E)
+    _rows_cols(act, "act", grouping.max_rows, I)
+    if _tensor(topk_w, "topk_w").numel() != num_tokens * top_k:
+        raise ValueError(f"topk_w must have {num_tokens * top_k} elements, got {topk_w.numel()}")
+    if y is not None:
+        _shape(y, "y", (num_tokens * top_k, H))
     act = _gpu(act, "act")
     dev = act.device
     w_down = _gpu(w_down, "w_down", act.dtype, dev)
     topk_w = _gpu(topk_w, "topk_w", torch.float32, dev)
-    E, H, I = w_down.shape
     p = problem(num_tokens, H, E, top_k, I, 0, act.dtype, weight_layout=weight_layout)
     if y is None:
         y = torch.empty((num_tokens * top_k, H), dtype=act.dtype, device=dev)
+    _gpu(y, "y", act.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_down(ctypes.byref(p), _ptr(act), _ptr(w_down), _ptr(topk_w),
                                        _ptr(grouping.sorted_pairs), _ptr(grouping.tile_expert),
@@ -288,18 +378,23 @@ def moe_down(act, w_down, topk_w, grouping: Grouping, num_tokens: int, top_k: in
 def moe_gate_up_ids(x, w_gate_up, topk_ids, act=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """act [N*k, I] in x.dtype, indexed by pair: act[p] = SwiGLU of x[p / k]
     through expert topk_ids[p] (no grouping needed; bf16, 4 <= N*k <= 1024)."""
+    N, H = _rank(x, "x", 2).shape
+    E, two_i, H2 = _rank(w_gate_up, "w_gate_up", 3).shape
+    if H2 != H or two_i % 2:
+        raise ValueError(f"w_gate_up must have shape (E, 2I, {H}), got {tuple(w_gate_up.shape)}")
+    if _rank(topk_ids, "topk_ids", 2).shape[0] != N:
+        raise ValueError(f"topk_ids must have shape ({N}, k), got {tuple(topk_ids.shape)}")
+    k = topk_ids.shape[1]
+    if act is not None:
+        _rows_cols(act, "act", N * k, two_i // 2)
     x = _gpu(x, "x")
     dev = x.device
     w_gate_up = _gpu(w_gate_up, "w_gate_up", x.dtype, dev)
     topk_ids = _gpu(topk_ids, "topk_ids", torch.int32, dev)
-    N, H = x.shape
-    E, two_i, _ = w_gate_up.shape
-    if topk_ids.dim() != 2 or topk_ids.shape[0] != N:
-        raise ValueError("topk_ids must be [N, k]")
-    k = topk_ids.shape[1]
     p = problem(N, H, E, k, two_i // 2, 0, x.dtype, weight_layout=weight_layout)
     if act is None:
         act = torch.empty((N * k, two_i // 2), dtype=x.dtype, device=dev)
+    _gpu(act, "act", x.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_gate_up_ids(ctypes.byref(p), _ptr(x), _ptr(w_gate_up), _ptr(topk_ids), _ptr(act),
                                               _stream(dev)))
@@ -308,18 +403,21 @@ def moe_gate_up_ids(x, w_gate_up, topk_ids, act=None, weight_layout=MOE_LAYOUT_R
 
 def moe_down_ids(act, w_down, topk_ids, topk_w, y=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """y [N*k, H] in act.dtype: y[p] = topk_w[p] * (act[p] . w_down[topk_ids[p]]^T)."""
+    E, H, I = _rank(w_down, "w_down", 3).shape
+    N, k = _rank(topk_ids, "topk_ids", 2).shape
+    _rows_cols(act, "act", N * k, I)
+    _shape(topk_w, "topk_w", (N, k))
+    if y is not None:
+        _shape(y, "y", (N * k, H))
     act = _gpu(act, "act")
     dev = act.device
     w_down = _gpu(w_down, "w_down", act.dtype, dev)
     topk_ids = _gpu(topk_ids, "topk_ids", torch.int32, dev)
     topk_w = _gpu(topk_w, "topk_w", torch.float32, dev)
-    E, H, I = w_down.shape
-    if topk_ids.dim() != 2:
-        raise ValueError("topk_ids must be [N, k]")
-    N, k = topk_ids.shape
     p = problem(N, H, E, k, I, 0, act.dtype, weight_layout=weight_layout)
     if y is None:
         y = torch.empty((N * k, H), dtype=act.dtype, device=dev)
+    _gpu(y, "y", act.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_down_ids(ctypes.byref(p), _ptr(act), _ptr(w_down), _ptr(topk_ids), _ptr(topk_w),
                                            _ptr(y), _stream(dev)))
@@ -329,18 +427,29 @@ def moe_down_ids(act, w_down, topk_ids, topk_w, y=None, weight_layout=MOE_LAYOUT
 def moe_shared_expert(x, shared_w_gate_up, shared_w_down, shared_scale, shared_act=None, shared_y=None,
                       weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """(shared_act [N, I_s], shared_y [N, H] = shared_scale[:, None] * SwiGLU_s(x))."""
+    N, H = _rank(x, "x", 2).shape
+    Is2, H2 = _rank(shared_w_gate_up, "shared_w_gate_up", 2).shape
+    if H2 != H or Is2 % 2:
+        raise ValueError(f"shared_w_gate_up must have shape (2I_s, {H}), got {tuple(shared_w_gate_up.shape)}")
+    Is = Is2 // 2
+    _shape(shared_w_down, "shared_w_down", (H, Is))
+    _shape(shared_scale, "shared_scale", (N,))
+    if shared_act is not None:
+        _shape(shared_act, "shared_act", (N, Is))
+    if shared_y is not None:
+        _shape(shared_y, "shared_y", (N, H))
     x = _gpu(x, "x")
     dev = x.device
     shared_w_gate_up = _gpu(shared_w_gate_up, "shared_w_gate_up", x.dtype, dev)
     shared_w_down = _gpu(shared_w_down, "shared_w_down", x.dtype, dev)
     shared_scale = _gpu(shared_scale, "shared_scale", torch.float32, dev)
-    N, H = x.shape
-    Is = shared_w_gate_up.shape[0] // 2
     p = problem(N, H, 1, 1, 1, Is, x.dtype, weight_layout=weight_layout)
     if shared_act is None:
         shared_act = torch.empty((N, Is), dtype=x.dtype, device=dev)
     if shared_y is None:
         shared_y = torch.empty((N, H), dtype=x.dtype, device=dev)
+    _gpu(shared_act, "shared_act", x.dtype, dev)
+    _gpu(shared_y, "shared_y", x.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_shared_expert(ctypes.byref(p), _ptr(x), _ptr(shared_w_gate_up),
                                                 _ptr(shared_w_down), _ptr(shared_scale), _ptr(shared_act),
@@ -350,14 +459,20 @@ def moe_shared_expert(x, shared_w_gate_up, shared_w_down, shared_scale, shared_a
 
 def moe_combine(y, num_tokens: int, top_k: int, shared_y=None, out=None):
     """out [N, H] = sum over the k slot rows of y (+ shared_y)."""
+    H = _rank(y, "y", 2).shape[1]
+    _shape(y, "y", (num_tokens * top_k, H))
+    if shared_y is not None:
+        _shape(shared_y, "shared_y", (num_tokens, H))
+    if out is not None:
+        _shape(out, "out", (num_tokens, H))
     y = _gpu(y, "y")
     dev = y.device
-    H = y.shape[1]
     if shared_y is not None:
         shared_y = _gpu(shared_y, "shared_y", y.dtype, dev)
     p = problem(num_tokens, H, top_k, top_k, 1, 0, y.dtype)
     if out is None:
         out = torch.empty((num_tokens, H), dtype=y.dtype, device=dev)
+    _gpu(out, "out", y.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_combine(ctypes.byref(p), _ptr(y), _ptr(shared_y), _ptr(out), _stream(dev)))
     return out
@@ -367,24 +482,27 @@ def moe_dense_mlp(x, w_gate_up, w_down, act=None, out=None, weight_layout=MOE_LA
     """Dense SwiGLU layer: out [N, H] = (silu(x Wg^T) * (x Wu^T)) Wd^T, with
     w_gate_up [2I, H] (gate rows first) and w_down [H, I]; act [N, I] is the
     intermediate (allocated when not given)."""
+    N, H = _rank(x, "x", 2).shape
+    two_i, H2 = _rank(w_gate_up, "w_gate_up", 2).shape
+    if H2 != H or two_i % 2:
+        raise ValueError(f"w_gate_up must have shape (2I, {H}), got {tuple(w_gate_up.shape)}")
+    I = two_i // 2
+    _shape(w_down, "w_down", (H, I))
+    if act is not None:
+        _shape(act, "act", (N, I))
+    if out is not None:
+        _shape(out, "out", (N, H))
     x = _gpu(x, "x")
     dev = x.device
     w_gate_up = _gpu(w_gate_up, "w_gate_up", x.dtype, dev)
     w_down = _gpu(w_down, "w_down", x.dtype, dev)
-    N, H = x.shape
-    two_i, H2 = w_gate_up.shape
-    if H2 != H or two_i % 2 or tuple(w_down.shape) != (H, two_i // 2):
-        raise ValueError("shape mismatch between x, w_gate_up and w_down")
-    I = two_i // 2
     p = problem(N, H, 1, 1, I, 0, x.dtype, weight_layout=weight_layout)
     if act is None:
         act = torch.empty((N, I), dtype=x.dtype, device=dev)
     if out is None:
         out = torch.empty_like(x)
-    for t, n, shape in ((act, "act", (N, I)), (out, "out", (N, H))):
-        _gpu(t, n, x.dtype, dev)
-        if tuple(t.shape) != shape:
-            raise ValueError(f"{n} must have shape {shape}")
+    _gpu(act, "act", x.dtype, dev)
+    _gpu(out, "out", x.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_dense_mlp(ctypes.byref(p), _ptr(x), _ptr(w_gate_up), _ptr(w_down), _ptr(act),
                                             _ptr(out), _stream(dev)))
@@ -395,26 +513,25 @@ def moe_add_rmsnorm(x, residual, weight, eps=1e-6, residual_out=None, normed=Non
     """(normed, residual_out): residual_out = x + residual (x when residual is
     None), normed = RMSNorm(residual_out) * weight.  residual_out may be
     `residual` itself (in place)."""
+    N, H = _rank(x, "x", 2).shape
+    for t, n in ((residual, "residual"), (residual_out, "residual_out"), (normed, "normed")):
+        if t is not None:
+            _shape(t, n, (N, H))
+    if _tensor(weight, "weight").numel() != H:
+        raise ValueError(f"weight must have {H} elements, got {weight.numel()}")
     x = _gpu(x, "x")
     dev = x.device
     if x.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {x.dtype}")
-    N, H = x.shape
     if residual is not None:
         _gpu(residual, "residual", x.dtype, dev)
-        if residual.shape != x.shape:
-            raise ValueError("residual must have the shape of x")
     weight = _gpu(weight, "weight", x.dtype, dev)
-    if weight.numel() != H:
-        raise ValueError("weight must have H elements")
     if residual_out is None:
         residual_out = torch.empty_like(x)
     if normed is None:
         normed = torch.empty_like(x)
-    for t, n in ((residual_out, "residual_out"), (normed, "normed")):
-        _gpu(t, n, x.dtype, dev)
-        if t.shape != x.shape:
-            raise ValueError(f"{n} must have the shape of x")
+    _gpu(residual_out, "residual_out", x.dtype, dev)
+    _gpu(normed, "normed", x.dtype, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_add_rmsnorm(N, H, _DTYPES[x.dtype], _ptr(x), _ptr(residual), _ptr(residual_out),
                                               _ptr(weight), float(eps), _ptr(normed), _stream(dev)))
@@ -435,11 +552,38 @@ def workspace_for(p: MoEProblem, device) -> torch.Tensor:
     return ws
 
 
+def _check_forward_shapes(x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out):
+    """Shapes of every tensor of the whole block, against x [N, H] and
+    w_gate_up [E, 2I, H]; raises ValueError before any device use."""
+    N, H = _rank(x, "x", 2).shape
+    E, two_i, H2 = _rank(w_gate_up, "w_gate_up", 3).shape
+    if H2 != H or two_i % 2:
+        raise ValueError(f"w_gate_up must have shape (E, 2I, {H}), got {tuple(w_gate_up.shape)}")
+    _shape(router_w, "router_w", (E, H))
+    _shape(w_down, "w_down", (E, H, two_i // 2))
+    given = [t is not None for t in (shared_w_gate_up, shared_w_down, shared_gate)]
+    if any(given) and not all(given):
+        raise ValueError("the shared expert needs shared_w_gate_up, shared_w_down and shared_gate together")
+    if shared_w_gate_up is not None:
+        Is2, H3 = _rank(shared_w_gate_up, "shared_w_gate_up", 2).shape
+        if H3 != H or Is2 % 2:
+            raise ValueError(f"shared_w_gate_up must have shape (2I_s, {H}), got {tuple(shared_w_gate_up.shape)}")
+        _shape(shared_w_down, "shared_w_down", (H, Is2 // 2))
+        if _tensor(shared_gate, "shared_gate").numel() != H:
+            raise ValueError(f"shared_gate must have {H} elements, got {shared_gate.numel()}")
+    if out is not None:
+        _shape(out, "out", (N, H))
+
+
 def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob=True, shared_w_gate_up=None,
                 shared_w_down=None, shared_gate=None, out=None, workspace=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """The whole block: out [N, H] in x.dtype.  With weight_layout
     MOE_LAYOUT_BLOCKED the expert (and shared-expert) weights are the
     outputs of moe_pack_weights."""
+    _check_forward_shapes(x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out)
+    p = problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up, weight_layout)
+    if workspace is not None:
+        _numel_at_least(workspace, "workspace", moe_workspace_size(p))
     x = _gpu(x, "x")
     dev = x.device
     for t, n in ((router_w, "router_w"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
@@ -448,11 +592,12 @@ def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob=True, shar
                  (shared_gate, "shared_gate")):
         if t is not None:
             _gpu(t, n, x.dtype, dev)
-    p = problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up, weight_layout)
     if out is None:
         out = torch.empty_like(x)
+    _gpu(out, "out", x.dtype, dev)
     if workspace is None:
         workspace = workspace_for(p, dev)
+    _gpu(workspace, "workspace", torch.uint8, dev)
     with torch.cuda.device(dev):
         _check(load_library().moe_forward(ctypes.byref(p), _ptr(x), _ptr(router_w), _ptr(w_gate_up), _ptr(w_down),
                                           _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(shared_gate),

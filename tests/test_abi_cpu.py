@@ -190,3 +190,145 @@ def test_forward_schedule_choice():
     assert L(5, 128, 4, 3, 64) == 0                     # 15 pairs: not a multiple of 4
     assert L(4, 128, 6, 2, 64) == 0                     # 8 pairs: 2 * 8 < 3 * 6
     assert L(6, 128, 6, 2, 64) == 1                     # 12 pairs: 2 * 12 >= 3 * 6
+
+
+# ------------------------------------------------- binding shape checks (no GPU)
+# Every binding checks each tensor's shape against the problem before it looks
+# at devices or launches anything.  On the CPU, a call whose shapes are right
+# stops at the device check ("must be on a GPU"); each wrong shape must stop
+# earlier, naming the tensor.
+
+import torch  # noqa: E402
+
+_N, _H, _E, _K, _I, _IS = 6, 64, 4, 2, 128, 192
+
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _expect(fn, *names):
+    """fn raises ValueError before the device check, naming one of `names`
+    (a disagreement between two tensors may name either)."""
+    with pytest.raises(ValueError) as ei:
+        fn()
+    msg = str(ei.value)
+    assert any(n in msg for n in names) and "on a GPU" not in msg, msg
+
+
+def _expect_device_error(fn):
+    with pytest.raises(ValueError, match="must be on a GPU"):
+        fn()
+
+
+def _grouping(P, E=_E, bm=16):
+    rows, tiles = moe.moe_align_capacity(P, E, bm)
+    i = dict(dtype=torch.int32)
+    return B.Grouping(_t(E, **i), _t(E + 1, **i), _t(P, **i), _t(rows, **i), _t(tiles, **i), _t(tiles, **i),
+                      _t(1, **i), bm, rows, tiles, E, P)
+
+
+def _forward_args():
+    return dict(x=_t(_N, _H), router_w=_t(_E, _H), w_gate_up=_t(_E, 2 * _I, _H), w_down=_t(_E, _H, _I),
+                top_k=_K, shared_w_gate_up=_t(2 * _IS, _H), shared_w_down=_t(_H, _IS), shared_gate=_t(_H),
+                out=_t(_N, _H))
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("x", _t(_N, _H + 64)), ("x", _t(_N * _H)), ("router_w", _t(_E + 1, _H)), ("w_gate_up", _t(_E, 2 * _I, _H + 64)),
+    ("w_gate_up", _t(_E, 2 * _I + 1, _H)), ("w_down", _t(_E, _H, _I + 64)), ("w_down", _t(_E, _I, _H)),
+    ("w_down", _t(_E + 1, _H, _I)), ("shared_w_gate_up", _t(2 * _IS, _H + 64)), ("shared_w_down", _t(_IS, _H)),
+    ("shared_w_down", _t(_H, _IS + 64)), ("shared_gate", _t(_H + 1)), ("out", _t(_N + 1, _H))])
+def test_forward_rejects_each_wrong_shape(name, bad):
+    a = _forward_args()
+    _expect_device_error(lambda: moe.moe_forward(**a))
+    a[name] = bad
+    _expect(lambda: moe.moe_forward(**a), name, "w_gate_up")
+
+
+def test_forward_rejects_partial_shared_expert():
+    a = _forward_args()
+    a["shared_gate"] = None
+    _expect(lambda: moe.moe_forward(**a), "shared")
+
+
+def test_forward_rejects_short_workspace():
+    a = _forward_args()
+    p = moe.problem(_N, _H, _E, _K, _I, _IS)
+    a["workspace"] = _t(moe.moe_workspace_size(p) - 1, dtype=torch.uint8)
+    _expect(lambda: moe.moe_forward(**a), "workspace")
+
+
+def test_route_rejects_wrong_shapes():
+    i32, f32 = torch.int32, torch.float32
+    ok = dict(x=_t(_N, _H), router_w=_t(_E, _H), top_k=_K, norm_topk_prob=True, shared_gate=_t(_H),
+              topk_ids=_t(_N, _K, dtype=i32), topk_w=_t(_N, _K, dtype=f32), shared_scale=_t(_N, dtype=f32))
+    _expect_device_error(lambda: moe.moe_route(**ok))
+    for name, bad in (("router_w", _t(_E, _H + 64)), ("shared_gate", _t(_H - 1)), ("topk_ids", _t(_N, _K + 1, dtype=i32)),
+                      ("topk_w", _t(_N + 1, _K, dtype=f32)), ("shared_scale", _t(_N + 1, dtype=f32)),
+                      ("scratch", _t(1, dtype=f32))):
+        a = dict(ok, **{name: bad})
+        _expect(lambda: moe.moe_route(**a), name)
+
+
+def test_align_rejects_wrong_shapes():
+    _expect(lambda: moe.moe_align(_t(_N * _K, dtype=torch.int32), _E, 16), "topk_ids")
+    big = 1200                                         # more than one 4096-pair chunk: needs scratch
+    _expect(lambda: moe.moe_align(_t(big, 4, dtype=torch.int32), _E, 16, scratch=_t(1, dtype=torch.int32)),
+            "scratch")
+
+
+def test_gate_up_and_down_reject_wrong_shapes():
+    g = _grouping(_N * _K)
+    x, wgu, wd = _t(_N, _H), _t(_E, 2 * _I, _H), _t(_E, _H, _I)
+    act, tw, y = _t(g.max_rows, _I), _t(_N, _K, dtype=torch.float32), _t(_N * _K, _H)
+    _expect_device_error(lambda: moe.moe_gate_up(x, wgu, g, _K, act))
+    _expect_device_error(lambda: moe.moe_down(act, wd, tw, g, _N, _K, y))
+    _expect(lambda: moe.moe_gate_up(_t(_N, _H + 64), wgu, g, _K, act), "w_gate_up", "x")
+    _expect(lambda: moe.moe_gate_up(x, wgu, g, _K, _t(g.max_rows - 1, _I)), "act")
+    _expect(lambda: moe.moe_gate_up(x, wgu, g, _K, _t(g.max_rows, _I + 64)), "act")
+    _expect(lambda: moe.moe_gate_up(x, wgu, _grouping(_N * _K + 2), _K, act), "grouping")
+    _expect(lambda: moe.moe_gate_up(x, _t(_E + 1, 2 * _I, _H), g, _K, act), "grouping")
+    _expect(lambda: moe.moe_down(_t(g.max_rows, _I + 64), wd, tw, g, _N, _K, y), "act")
+    _expect(lambda: moe.moe_down(act, _t(_E, _H, _I + 64), tw, g, _N, _K, y), "act")
+    _expect(lambda: moe.moe_down(act, wd, _t(_N, _K + 1, dtype=torch.float32), g, _N, _K, y), "topk_w")
+    _expect(lambda: moe.moe_down(act, wd, tw, g, _N, _K, _t(_N * _K, _H + 64)), "y")
+    _expect(lambda: moe.moe_down(act, wd, tw, g, _N + 1, _K, y), "grouping")
+
+
+def test_ids_products_reject_wrong_shapes():
+    x, wgu, wd = _t(_N, _H), _t(_E, 2 * _I, _H), _t(_E, _H, _I)
+    ids, tw = _t(_N, _K, dtype=torch.int32), _t(_N, _K, dtype=torch.float32)
+    act, y = _t(_N * _K, _I), _t(_N * _K, _H)
+    _expect_device_error(lambda: moe.moe_gate_up_ids(x, wgu, ids, act))
+    _expect_device_error(lambda: moe.moe_down_ids(act, wd, ids, tw, y))
+    _expect(lambda: moe.moe_gate_up_ids(x, wgu, _t(_N + 1, _K, dtype=torch.int32), act), "topk_ids")
+    _expect(lambda: moe.moe_gate_up_ids(x, wgu, ids, _t(_N * _K - 1, _I)), "act")
+    _expect(lambda: moe.moe_gate_up_ids(x, _t(_E, 2 * _I, _H - 64), ids, act), "w_gate_up")
+    _expect(lambda: moe.moe_down_ids(_t(_N * _K, _I + 64), wd, ids, tw, y), "act")
+    _expect(lambda: moe.moe_down_ids(act, wd, ids, _t(_N * _K, dtype=torch.float32), y), "topk_w")
+    _expect(lambda: moe.moe_down_ids(act, wd, ids, tw, _t(_N * _K, _H - 64)), "y")
+
+
+def test_shared_combine_dense_norm_reject_wrong_shapes():
+    x, sgu, sdn, sc = _t(_N, _H), _t(2 * _IS, _H), _t(_H, _IS), _t(_N, dtype=torch.float32)
+    _expect_device_error(lambda: moe.moe_shared_expert(x, sgu, sdn, sc))
+    _expect(lambda: moe.moe_shared_expert(x, sgu, _t(_IS, _H), sc), "shared_w_down")
+    _expect(lambda: moe.moe_shared_expert(x, sgu, sdn, _t(_N + 1, dtype=torch.float32)), "shared_scale")
+    _expect(lambda: moe.moe_shared_expert(x, sgu, sdn, sc, shared_act=_t(_N, _IS + 64)), "shared_act")
+    _expect(lambda: moe.moe_shared_expert(x, sgu, sdn, sc, shared_y=_t(_N, _H + 64)), "shared_y")
+    y = _t(_N * _K, _H)
+    _expect_device_error(lambda: moe.moe_combine(y, _N, _K))
+    _expect(lambda: moe.moe_combine(_t(_N * _K - 1, _H), _N, _K), "y")
+    _expect(lambda: moe.moe_combine(y, _N, _K, shared_y=_t(_N, _H + 64)), "shared_y")
+    _expect(lambda: moe.moe_combine(y, _N, _K, out=_t(_N + 1, _H)), "out")
+    gu, dn = _t(2 * _I, _H), _t(_H, _I)
+    _expect_device_error(lambda: moe.moe_dense_mlp(x, gu, dn))
+    _expect(lambda: moe.moe_dense_mlp(x, gu, _t(_I, _H)), "w_down")
+    _expect(lambda: moe.moe_dense_mlp(x, gu, dn, act=_t(_N, _I + 64)), "act")
+    _expect(lambda: moe.moe_dense_mlp(x, gu, dn, out=_t(_N, _H + 64)), "out")
+    w = _t(_H)
+    _expect_device_error(lambda: moe.moe_add_rmsnorm(x, x, w))
+    _expect(lambda: moe.moe_add_rmsnorm(x, _t(_N, _H + 64), w), "residual")
+    _expect(lambda: moe.moe_add_rmsnorm(x, x, _t(_H + 8)), "weight")
+    _expect(lambda: moe.moe_add_rmsnorm(x, x, w, normed=_t(_N + 1, _H)), "normed")

@@ -47,7 +47,7 @@ def test_oracle_formulations_agree(s):
     args = (h["x"], h["router_w"], h["w_gate_up"], h["w_down"], cfg.top_k, cfg.norm_topk_prob)
     a, _ = O.moe_forward(*args, shared=sh)
     b, _, _ = O.moe_forward_grouped(*args, shared=sh)
-    c = O.moe_forward_masked(*args, shared=sh)
+    c = O.moe_forward_by_slot(*args, shared=sh)
     scale = max(1.0, float(np.abs(a).max()))
     assert np.abs(a - b).max() <= 1e-12 * scale
     assert np.abs(a - c).max() <= 1e-12 * scale

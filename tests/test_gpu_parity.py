@@ -59,6 +59,19 @@ def compare_routing(h, cfg, ids_gpu, w_gpu):
     return (ids_ref, w_ref, probs, margin), keep
 
 
+def full_reference(h, hw, sh, cfg, routing, sample):
+    """The oracle's output for every token, in the grouped formulation (one
+    float64 product per expert over its gathered tokens, then index-add),
+    after checking it against the per-token definition on `sample` rows."""
+    ref, _, _ = O.moe_forward_grouped(h["x"], h["router_w"], hw["w_gate_up"], hw["w_down"], cfg.top_k,
+                                      cfg.norm_topk_prob, shared=sh, routing=routing)
+    defn, _ = O.moe_forward(h["x"], h["router_w"], hw["w_gate_up"], hw["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                            shared=sh, rows=sample, routing=routing)
+    scale = max(1.0, float(np.abs(defn).max()))
+    assert np.abs(ref[sample] - defn).max() <= 1e-12 * scale, "grouped oracle differs from the definition"
+    return ref
+
+
 def check_output(out_rows, ref_rows, dtype, what=""):
     tol = O.tolerance(ref_rows, dtype)
     err = float(np.abs(out_rows - ref_rows).max()) if ref_rows.size else 0.0
@@ -246,18 +259,18 @@ def test_full_size_parity(name):
         drop[n * k:(n + 1) * k] = True
     order_g = gr.order.cpu().numpy()
     assert np.array_equal(order_g[~drop[order_g]], order_r[~drop[order_r]])
-    # outputs on sampled tokens
+    # outputs: every token the margin rule keeps, element by element
     rng = np.random.default_rng(5)
-    rows = sorted(set([0, cfg.N - 1] + rng.choice(cfg.N, size=min(cfg.N, 22), replace=False).tolist()))
-    rows = [r for r in rows if keep[r]]
+    sample = sorted(set([0, cfg.N - 1] + rng.choice(cfg.N, size=min(cfg.N, 6), replace=False).tolist()))
     hw = {"w_gate_up": host(t["w_gate_up"]), "w_down": host(t["w_down"])}
+    h["x"] = host(t["x"])
     sh = None
     if cfg.I_shared:
         sh = {"w_gate_up": host(t["shared_w_gate_up"]), "w_down": host(t["shared_w_down"]),
               "gate": host(t["shared_gate"])}
-    ref, _ = O.moe_forward(h["x"], h["router_w"], hw["w_gate_up"], hw["w_down"], k, cfg.norm_topk_prob,
-                           shared=sh, rows=rows, routing=routing)
-    err, tol = check_output(host(out)[rows], ref, cfg.dtype, name)
+    ref = full_reference(h, hw, sh, cfg, routing, sample)
+    err, tol = check_output(host(out)[keep], ref[keep], cfg.dtype, name)
+    print(f"{name}: all {int(keep.sum())} kept rows compared")
     nz = int((counts_r == 0).sum())
     print(f"{name}: err {err:.3e} tol {tol:.3e} excluded tokens {excluded.size} "
           f"counts min/max {counts_r.min()}/{counts_r.max()} empty experts {nz}")
@@ -271,8 +284,7 @@ def test_larger_layer_shape(N):
     """A larger layer of the same family (H=4096, E=128, top-8, I=1536:
     twice the reduction length of both products and of the router).  64
     tokens take the ids products, 1024 and 4096 the grouped tiles.  Routing
-    is compared on every token and the output on sampled tokens; only the
-    experts those tokens use are copied to the host."""
+    and outputs are compared on every token."""
     cfg = random_case(N, 4096, 128, 8, 1536, dtype="bf16", seed=31)
     t = make_inputs(cfg, DEV)
     out = run_forward(t, cfg)
@@ -280,20 +292,11 @@ def test_larger_layer_shape(N):
     torch.cuda.synchronize()
     h = {"x": host(t["x"]), "router_w": host(t["router_w"])}
     (ids_ref, w_ref, probs, margin), keep = compare_routing(h, cfg, ids_gpu, w_gpu)
-    rng = np.random.default_rng(N)
-    rows = [int(r) for r in sorted(set([0, N - 1] + rng.choice(N, size=4, replace=False).tolist())) if keep[r]]
-    used = sorted({int(e) for r in rows for e in ids_ref[r]})
-    slot = {e: i for i, e in enumerate(used)}
-    sub_ids = np.zeros_like(ids_ref)
-    for r in rows:
-        sub_ids[r] = [slot[int(e)] for e in ids_ref[r]]
-    sel = torch.tensor(used, device=DEV)
-    wgu = host(t["w_gate_up"].index_select(0, sel))
-    wd = host(t["w_down"].index_select(0, sel))
-    ref, _ = O.moe_forward(h["x"], h["router_w"], wgu, wd, cfg.top_k, cfg.norm_topk_prob, rows=rows,
-                           routing=(sub_ids, w_ref, probs, margin))
-    err, tol = check_output(host(out)[rows], ref, cfg.dtype, cfg.name)
-    print(f"{cfg.name}: err {err:.3e} tol {tol:.3e} rows {len(rows)} experts {len(used)} "
+    hw = {"w_gate_up": host(t["w_gate_up"]), "w_down": host(t["w_down"])}
+    del t["w_gate_up"], t["w_down"]
+    ref = full_reference(h, hw, None, cfg, (ids_ref, w_ref, probs, margin), [0, N // 2, N - 1])
+    err, tol = check_output(host(out)[keep], ref[keep], cfg.dtype, cfg.name)
+    print(f"{cfg.name}: err {err:.3e} tol {tol:.3e} all {int(keep.sum())} kept rows, "
           f"excluded {int((~keep).sum())}")
 
 

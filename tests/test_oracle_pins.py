@@ -77,14 +77,6 @@ def test_grouping_pin_catches_repeat_mistake(monkeypatch):
     assert flat_tok.tolist() != g["flat_tok"]
 
 
-def test_grouping_pin_catches_unstable_sort():
-    g = golden("m03_grouping_walkthrough.json")
-    flat_e = np.array(g["flat_e"])
-    # A sort that does not keep ascending pair order inside a segment.
-    bad = np.lexsort((-np.arange(flat_e.size), flat_e))
-    assert bad.tolist() != g["order"]
-
-
 @pytest.mark.parametrize("seed", range(6))
 def test_group_invariants_and_stable_sort(seed):
     rng = np.random.default_rng(seed)
@@ -148,6 +140,25 @@ def test_route_example_both_modes():
         assert rnd(w, d) == g[key]
     _, w, _, _ = O.route(x, eye, g["top_k"], False)
     assert round(float(w[0].astype(np.float64).sum()), d) == g["weight_sum_no_renorm_token0"]
+
+
+def test_route_large_logits():
+    """Logits in the hundreds and thousands: the probabilities are still the
+    softmax of the logits (scipy's, in float64), which depends only on the
+    differences between logits, so exp never overflows; router = eye(4) makes
+    the logits equal to x ([M03] 题面速览: float32 softmax over all E)."""
+    x = np.array([[1000.0, 999.0, 990.0, 0.0], [-500.0, 300.0, 299.5, 120.0], [88.0, 89.0, 90.0, 91.0]],
+                 np.float32)
+    eye = np.eye(4, dtype=np.float32)
+    ids, w, probs, _ = O.route(x, eye, 2, False)
+    ref = scipy.special.softmax(x.astype(np.float64), axis=1)
+    assert np.isfinite(probs).all()
+    np.testing.assert_allclose(probs, ref, rtol=1e-6, atol=1e-12)
+    assert ids.tolist() == [[0, 1], [1, 2], [3, 2]]
+    np.testing.assert_allclose(w, np.take_along_axis(ref, ids, 1), rtol=1e-6)
+    _, w_on, _, _ = O.route(x, eye, 2, True)
+    sel = np.take_along_axis(x.astype(np.float64), ids, 1)
+    np.testing.assert_allclose(w_on, scipy.special.softmax(sel, axis=1), rtol=1e-6)
 
 
 def test_route_pin_catches_topk_before_softmax(monkeypatch):
@@ -244,7 +255,7 @@ def test_scalar_per_expert_table():
         assert rnd(ys, d) == g["per_expert_out"][key]
 
 
-@pytest.mark.parametrize("form", ["definition", "grouped", "masked"])
+@pytest.mark.parametrize("form", ["definition", "grouped", "by_slot"])
 def test_scalar_block_end_to_end(form):
     g = golden("m03_scalar_block.json")
     r, gu, wd = scalar_weights(g)
@@ -254,7 +265,7 @@ def test_scalar_block_end_to_end(form):
     elif form == "grouped":
         out, _, _ = O.moe_forward_grouped(x, r, gu, wd, g["top_k"], True)
     else:
-        out = O.moe_forward_masked(x, r, gu, wd, g["top_k"], True)
+        out = O.moe_forward_by_slot(x, r, gu, wd, g["top_k"], True)
     assert rnd(out, g["decimals"]) == g["out"]
 
 
@@ -302,13 +313,13 @@ def test_scalar_shared_expert():
     se = [float(O.swiglu(x[n], shared["w_gate_up"][:1], shared["w_gate_up"][1:], shared["w_down"])[0])
           for n in range(2)]
     assert rnd(se, d) == s["shared_expert_out"]
-    for form in ("definition", "grouped", "masked"):
+    for form in ("definition", "grouped", "by_slot"):
         if form == "definition":
             out, _ = O.moe_forward(x, r, gu, wd, g["top_k"], True, shared=shared)
         elif form == "grouped":
             out, _, _ = O.moe_forward_grouped(x, r, gu, wd, g["top_k"], True, shared=shared)
         else:
-            out = O.moe_forward_masked(x, r, gu, wd, g["top_k"], True, shared=shared)
+            out = O.moe_forward_by_slot(x, r, gu, wd, g["top_k"], True, shared=shared)
         assert rnd(out, d) == s["out_with_shared"]
 
 
@@ -340,15 +351,6 @@ def test_dense_special_case_matches_torch_swiglu():
         np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
 
 
-def test_swiglu_pin_catches_missing_transpose():
-    rng = np.random.default_rng(12)
-    h = rng.standard_normal((3, 6))
-    wg = rng.standard_normal((4, 6))
-    with pytest.raises(ValueError):
-        _ = h @ wg                                                          # [3,6] @ [4,6] does not fit
-    assert O.swiglu(h, wg, wg, rng.standard_normal((6, 4))).shape == (3, 6)
-
-
 # ------------------------------------------------------------- whole block
 
 @pytest.mark.parametrize("seed,shape", [(0, (7, 8, 6, 2, 5, 0)), (1, (11, 5, 4, 4, 3, 2)),
@@ -360,7 +362,7 @@ def test_three_formulations_agree(seed, shape):
     for renorm in (True, False):
         a, _ = O.moe_forward(x, r, gu, wd, k, renorm, shared=shared)
         b, _, _ = O.moe_forward_grouped(x, r, gu, wd, k, renorm, shared=shared)
-        c = O.moe_forward_masked(x, r, gu, wd, k, renorm, shared=shared)
+        c = O.moe_forward_by_slot(x, r, gu, wd, k, renorm, shared=shared)
         scale = np.abs(a).max()
         np.testing.assert_allclose(b, a, atol=1e-12 * scale)
         np.testing.assert_allclose(c, a, atol=1e-12 * scale)
@@ -495,20 +497,3 @@ def test_add_rmsnorm_residual_semantics():
     for n, r in ((n0, r0), (n1, r1)):
         ref = torch.nn.functional.rms_norm(torch.from_numpy(r).double(), (32,), torch.from_numpy(w), 1e-6)
         np.testing.assert_allclose(n, ref.numpy(), rtol=1e-12, atol=1e-12)
-
-
-def test_add_rmsnorm_pin_catches_norm_before_add(monkeypatch):
-    """Planted mistake: normalising the input before adding the residual."""
-    rng = np.random.default_rng(25)
-    x = rng.standard_normal((3, 16)).astype(np.float32)
-    res = (rng.standard_normal((3, 16)) * 4).astype(np.float32)
-    w = np.ones(16)
-
-    def wrong(x_, residual, weight, eps, dtype):
-        n = O.rms_norm(x_, weight, eps)
-        r = O.round_to((n + residual).astype(np.float32), dtype)
-        return O.rms_norm(r, weight, eps), r
-
-    monkeypatch.setattr(O, "add_rmsnorm", wrong)
-    _, r = O.add_rmsnorm(x, res, w, 1e-6, "f32")
-    assert not np.array_equal(r, (x + res).astype(np.float32))
