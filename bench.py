@@ -13,7 +13,13 @@ the 64-token decode layer, H=2048, E=128, top-8, I=768, bf16).  ``roofline``
 is for the dominant kernel of that workload, timed with HIP events on the
 stream the kernels run on, in a second loop that issues the same stages one
 by one.  ``cpu_baseline`` times the CPU oracle on a bounded token sample.
-``also`` holds the same figures for the other workloads given with --also.
+``also`` holds the same figures for the other workloads given with --also
+(by default the 4096-token prefill layer, the 16384-token skewed layer with
+its expert-load report, the 8192-token talker layer with a shared expert, a
+dense SwiGLU layer and the graph-replayed decode block), each timed over the
+same number of steps as the main workload.  Every step time is given as the
+wall-clock mean over the timed steps and as the median / min / mean of
+per-step HIP events.
 """
 from __future__ import annotations
 
@@ -27,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (datasheet, no sparsity)
 METRIC = "MoE-layer tokens/s; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 
 
@@ -37,11 +43,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "talker"])
-    ap.add_argument("--also", default="prefill,dense_prefill,decode_block",
+    ap.add_argument("--also", default="prefill,skew,talker,dense_prefill,decode_block",
                     help="comma-separated extra workloads ('' for none): prefill, skew, talker, decode, "
                          "dense_prefill, dense_decode (dense SwiGLU layers), decode_block (residual add + "
                          "RMSNorm + the decode MoE layer, eager and replayed from a HIP graph)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget (0: skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle budget: whole passes over the main workload on all cores for about this "
+                         "long, then a single-thread sample of a third of it (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -70,6 +78,54 @@ def kernel_work(cfg, counts):
     }
 
 
+def timed_steps(fn, steps, warmup, torch):
+    """Run `warmup` untimed steps, then exactly `steps` timed ones between two
+    device synchronisations.  Returns the wall-clock mean per step (ms) and
+    the per-step HIP-event durations (ms), recorded on torch's current stream
+    (the stream every call is enqueued on)."""
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return wall, per
+
+
+def event_summary(per):
+    n = len(per)
+    med = per[n // 2] if n % 2 else 0.5 * (per[n // 2 - 1] + per[n // 2])
+    return {"median": round(med, 5), "min": round(per[0], 5), "mean": round(sum(per) / n, 5)}
+
+
+def load_report(counts, cfg):
+    """Pairs per expert: min / max, experts with none, and the log-log slope
+    of count against rank over the experts that have pairs (least squares),
+    also over the ranks below the N-pair cap (where the Zipf target is not
+    cut off)."""
+    import numpy as np
+
+    c = np.sort(np.asarray(counts, dtype=np.float64))[::-1]
+    live = c[c > 0]
+    rank = np.arange(1, live.size + 1, dtype=np.float64)
+
+    def slope(v, r):
+        return float(np.polyfit(np.log(r), np.log(v), 1)[0]) if v.size >= 2 else None
+
+    below = live < cfg.N
+    return {"counts_min": int(c.min()), "counts_max": int(c.max()), "experts_with_no_pairs": int((c == 0).sum()),
+            "loglog_slope_live": round(slope(live, rank), 4),
+            "loglog_slope_below_cap": round(slope(live[below], rank[below]), 4),
+            "experts_at_cap": int((live >= cfg.N).sum()), "target_zipf_s": cfg.skew_s,
+            "counts_desc": [int(v) for v in c]}
+
+
 def bench_workload(name, steps, warmup, torch, moe):
     from sparse_moe_ffn_amd.inputs import CONFIGS, make_inputs
 
@@ -87,15 +143,9 @@ def bench_workload(name, steps, warmup, torch, moe):
                          t["shared_w_gate_up"], blk)
     ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device=dev)
     out = torch.empty_like(t["x"])
-    for _ in range(warmup):
-        moe.moe_forward(*args, out=out, workspace=ws, weight_layout=blk)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        moe.moe_forward(*args, out=out, workspace=ws, weight_layout=blk)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_row_major = timed(lambda: moe.moe_forward(*args_rm, out=out, workspace=ws), steps, warmup, torch)
+    wall, per = timed_steps(lambda: moe.moe_forward(*args, out=out, workspace=ws, weight_layout=blk),
+                            steps, warmup, torch)
+    ms_row_major, per_rm = timed_steps(lambda: moe.moe_forward(*args_rm, out=out, workspace=ws), steps, warmup, torch)
 
     # Same stages issued one by one, HIP events between them, on the stream
     # the kernels run on (torch's current stream).
@@ -155,17 +205,23 @@ def bench_workload(name, steps, warmup, torch, moe):
     torch.cuda.synchronize()
     stage_ms = {name_: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
                 for i, name_ in enumerate(stages)}
+    stage_median_ms = {name_: event_summary(sorted(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)))["median"]
+                       for i, name_ in enumerate(stages)}
     counts = moe.moe_align(ids, cfg.E, bm, align_scratch).counts.cpu().numpy()   # untimed: pairs per expert
     work = kernel_work(cfg, counts)
-    ms = elapsed / steps * 1e3
+    ms = wall
     res = {
         "cfg": cfg, "inputs": t, "ms_per_step": ms, "tokens_per_s": cfg.N / (ms * 1e-3),
-        "ms_per_step_row_major": ms_row_major,
-        "tflops": cfg.flops() / (ms * 1e-3) / 1e12, "stage_ms": stage_ms, "work": work,
-        "hit_experts": expert_hits(counts), "counts_min_max": [int(counts.min()), int(counts.max())],
-        "block_m": bm, "ids_path": ids_path,
+        "step_event_ms": event_summary(per), "ms_per_step_row_major": ms_row_major,
+        "step_event_ms_row_major": event_summary(per_rm),
+        "tflops": cfg.flops() / (ms * 1e-3) / 1e12, "stage_ms": stage_ms, "stage_median_ms": stage_median_ms,
+        "work": work, "hit_experts": expert_hits(counts), "counts_min_max": [int(counts.min()), int(counts.max())],
+        "block_m": bm, "ids_path": ids_path, "counts": counts, "steps": steps,
     }
+    med = res["step_event_ms"]["median"]
+    res["tflops_median"] = cfg.flops() / (med * 1e-3) / 1e12
     res["mfma_frac"] = res["tflops"] / MFMA_BF16_PEAK_TFLOPS
+    res["mfma_frac_median"] = res["tflops_median"] / MFMA_BF16_PEAK_TFLOPS
     weight_bytes = res["hit_experts"] * 3 * cfg.I * cfg.H * 2 + cfg.I_shared * 3 * cfg.H * 2
     res["weight_hbm_frac"] = weight_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
     return res
@@ -189,17 +245,6 @@ def prewarm(torch, moe, seconds=1.0):
     torch.cuda.empty_cache()
 
 
-def timed(fn, steps, warmup, torch):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fn()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e3
-
-
 def bench_dense(name, steps, warmup, torch, moe):
     """A dense SwiGLU layer (moe_dense_mlp) of hidden 2048, I = 6144."""
     from sparse_moe_ffn_amd.inputs import DENSE_LAYERS, make_dense_inputs
@@ -209,13 +254,13 @@ def bench_dense(name, steps, warmup, torch, moe):
     act = torch.empty((L["N"], L["I"]), dtype=t["x"].dtype, device="cuda:0")
     out = torch.empty_like(t["x"])
     wgu, wd = moe.moe_pack_weights(t["w_gate_up"]), moe.moe_pack_weights(t["w_down"])
-    ms = timed(lambda: moe.moe_dense_mlp(t["x"], wgu, wd, act=act, out=out, weight_layout=moe.MOE_LAYOUT_BLOCKED),
-               steps, warmup, torch)
+    ms, per = timed_steps(lambda: moe.moe_dense_mlp(t["x"], wgu, wd, act=act, out=out,
+                                                    weight_layout=moe.MOE_LAYOUT_BLOCKED), steps, warmup, torch)
     flops = 6.0 * L["N"] * L["H"] * L["I"]
     wbytes = 3 * L["H"] * L["I"] * 2
     return {"workload": f"{name}: dense SwiGLU layer N={L['N']} H={L['H']} I={L['I']} bf16",
-            "tokens_per_s": round(L["N"] / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "steps": steps, "tokens_per_s": round(L["N"] / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "step_event_ms": event_summary(per), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "weight_hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -238,17 +283,18 @@ def bench_decode_block(steps, warmup, torch, moe):
         moe.moe_forward(normed, t["router_w"], wgu, wd, cfg.top_k, cfg.norm_topk_prob,
                         out=out, workspace=ws, weight_layout=moe.MOE_LAYOUT_BLOCKED)
 
-    eager = timed(block, steps, warmup, torch)
+    eager, per_e = timed_steps(block, steps, warmup, torch)
     block()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         block()
-    replay = timed(graph.replay, steps, warmup, torch)
+    replay, per_g = timed_steps(graph.replay, steps, warmup, torch)
     del graph
     return {"workload": "decode_block: residual add + RMSNorm + the 64-token decode MoE layer",
-            "tokens_per_s": round(cfg.N / (replay * 1e-3), 1), "ms_per_step_graph": round(replay, 4),
-            "ms_per_step_eager": round(eager, 4)}
+            "steps": steps, "tokens_per_s": round(cfg.N / (replay * 1e-3), 1), "ms_per_step_graph": round(replay, 4),
+            "step_event_ms_graph": event_summary(per_g), "ms_per_step_eager": round(eager, 4),
+            "step_event_ms_eager": event_summary(per_e)}
 
 
 GEMM_SOURCES = ("sparse_moe_ffn_amd/csrc/grouped_gemm.hip", "sparse_moe_ffn_amd/csrc/moe_common.h",
@@ -312,40 +358,73 @@ def roofline_for(res):
             "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(res, budget_s, torch):
-    """The CPU oracle, as it is, on the first tokens of the same workload
-    until the time budget is spent (routing of the whole batch included)."""
+    """The CPU oracle as it is (its per-token definition, numpy float64 expert
+    math) on the main workload, run on the host cores: the routing of the
+    whole batch, then the tokens split over one worker thread per core (at
+    most 16, the host share of one GPU), each with one BLAS thread.  Whole
+    passes over the batch until the budget is spent.  Then the same oracle on
+    one thread over the first tokens of the batch for a third of the budget."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
     from oracle import moe_oracle as O
 
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:                                # no way to pin BLAS threads: one worker
+        threadpool_limits = None
     cfg, t = res["cfg"], res["inputs"]
     h = {k: (v.float().cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
     sh = None
     if cfg.I_shared:
         sh = {"w_gate_up": h["shared_w_gate_up"], "w_down": h["shared_w_down"], "gate": h["shared_gate"]}
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS default
-        cores = os.cpu_count()
-    # Whole passes over the batch (routing of every token, then the expert
-    # math token by token) until the budget is spent; a pass that does not
-    # fit the budget stops at the token where the budget ran out.
-    t0 = time.perf_counter()
-    done = passes = 0
-    while (time.perf_counter() - t0) < budget_s:
+    cores = len(os.sched_getaffinity(0))
+    workers = min(cores, 16) if threadpool_limits else 1
+
+    def forward(rows, routing):
+        O.moe_forward(h["x"], h["router_w"], h["w_gate_up"], h["w_down"], cfg.top_k, cfg.norm_topk_prob,
+                      shared=sh, rows=rows, routing=routing)
+
+    def one_pass(pool):
         routing = O.route(h["x"], h["router_w"], cfg.top_k, cfg.norm_topk_prob)
-        n = 0
-        while n < cfg.N and (time.perf_counter() - t0) < budget_s:
-            O.moe_forward(h["x"], h["router_w"], h["w_gate_up"], h["w_down"], cfg.top_k, cfg.norm_topk_prob,
-                          shared=sh, rows=[n], routing=routing)
-            n += 1
-        done += n
-        passes += n == cfg.N
-    el = time.perf_counter() - t0
-    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} tokens of the {cfg.name} layer ({passes} whole passes over its {cfg.N} tokens, "
-                      f"each routing the whole batch), {el:.1f} s, numpy float64 expert math"}
+        chunks = [list(range(i, cfg.N, workers)) for i in range(min(workers, cfg.N))]
+        list(pool.map(lambda rows: forward(rows, routing), chunks))
+
+    import contextlib
+    limit = threadpool_limits(1) if threadpool_limits else contextlib.nullcontext()
+    with limit, ThreadPoolExecutor(workers) as pool:
+        t0 = time.perf_counter()
+        passes = 0
+        while passes == 0 or time.perf_counter() - t0 < budget_s:
+            one_pass(pool)
+            passes += 1
+        el = time.perf_counter() - t0
+        # single thread: routing of the whole batch, then tokens one by one
+        t1 = time.perf_counter()
+        routing = O.route(h["x"], h["router_w"], cfg.top_k, cfg.norm_topk_prob)
+        n1 = 0
+        while n1 < cfg.N and (n1 == 0 or time.perf_counter() - t1 < budget_s / 3):
+            forward([n1], routing)
+            n1 += 1
+        el1 = time.perf_counter() - t1
+    return {"value": round(passes * cfg.N / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "threads_used": workers, "cpu_model": _cpu_model(),
+            "single_thread": {"value": round(n1 / el1, 3), "unit": "tokens/s", "tokens": n1, "seconds": round(el1, 2)},
+            "sample": f"{passes} whole passes over the {cfg.N} tokens of the {cfg.name} layer in {el:.1f} s "
+                      f"(routing of the batch, then the per-token definition in numpy float64, tokens split over "
+                      f"{workers} threads with one BLAS thread each); single thread: the first {n1} tokens"}
 
 
 def copy_calibration(torch):
@@ -356,6 +435,26 @@ def copy_calibration(torch):
         b.copy_(a)
     torch.cuda.synchronize()
     return n
+
+
+def leg_summary(r):
+    """The figures of one MoE workload for the `also` part of the line."""
+    cfg = r["cfg"]
+    out = {"workload": f"{cfg.name}: N={cfg.N} H={cfg.H} E={cfg.E} top-{cfg.top_k} I={cfg.I}"
+                       + (f" shared I_s={cfg.I_shared}" if cfg.I_shared else "")
+                       + f" norm_topk_prob={cfg.norm_topk_prob}",
+           "steps": r["steps"], "tokens_per_s": round(r["tokens_per_s"], 1),
+           "ms_per_step": round(r["ms_per_step"], 4), "step_event_ms": r["step_event_ms"],
+           "ms_per_step_row_major": round(r["ms_per_step_row_major"], 4),
+           "step_event_ms_row_major": r["step_event_ms_row_major"],
+           "tflops": round(r["tflops"], 1), "mfma_frac": round(r["mfma_frac"], 4),
+           "mfma_frac_median": round(r["mfma_frac_median"], 4), "weight_hbm_frac": round(r["weight_hbm_frac"], 4),
+           "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
+           "stage_median_ms": r["stage_median_ms"], "roofline": roofline_for(r),
+           "counts_min_max": r["counts_min_max"], "hit_experts": r["hit_experts"]}
+    if cfg.skew:
+        out["load"] = load_report(r["counts"], cfg)
+    return out
 
 
 def main():
@@ -379,20 +478,15 @@ def main():
     for w in [s for s in a.also.split(",") if s and s != a.workload]:
         print(f"[bench] workload {w}", file=sys.stderr, flush=True)
         if w.startswith("dense_"):
-            also[w] = bench_dense(w, max(10, a.steps // 10), max(3, a.warmup // 4), torch, moe)
+            also[w] = bench_dense(w, a.steps, a.warmup, torch, moe)
             torch.cuda.empty_cache()
             continue
         if w == "decode_block":
             also[w] = bench_decode_block(a.steps, a.warmup, torch, moe)
             torch.cuda.empty_cache()
             continue
-        r = bench_workload(w, max(10, a.steps // 4), max(5, a.warmup // 2), torch, moe)
-        also[w] = {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 4),
-                   "ms_per_step_row_major": round(r["ms_per_step_row_major"], 4),
-                   "tflops": round(r["tflops"], 1), "mfma_frac": round(r["mfma_frac"], 4),
-                   "weight_hbm_frac": round(r["weight_hbm_frac"], 4),
-                   "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
-                   "roofline": roofline_for(r), "counts_min_max": r["counts_min_max"]}
+        r = bench_workload(w, a.steps, a.warmup, torch, moe)
+        also[w] = leg_summary(r)
         del r
         torch.cuda.empty_cache()
     if a.copy_calibration:
@@ -405,14 +499,17 @@ def main():
     line = {
         "metric": METRIC, "value": round(main_res["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(main_res["ms_per_step"], 5),
+        "step_event_ms": main_res["step_event_ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: Qwen3-30B-A3B-shaped MoE layer", "tokens": cfg.N, "hidden": cfg.H,
                    "experts": cfg.E, "top_k": cfg.top_k, "inter": cfg.I, "shared_inter": cfg.I_shared,
                    "norm_topk_prob": cfg.norm_topk_prob, "seed": cfg.seed, "weight_layout": "blocked"},
         "ms_per_step_row_major": round(main_res["ms_per_step_row_major"], 5),
+        "step_event_ms_row_major": main_res["step_event_ms_row_major"],
         "tflops": round(main_res["tflops"], 2), "mfma_frac": round(main_res["mfma_frac"], 4),
         "weight_hbm_frac": round(main_res["weight_hbm_frac"], 4),
         "stage_ms": {k: round(v, 4) for k, v in main_res["stage_ms"].items()},
+        "stage_median_ms": main_res["stage_median_ms"],
         "hit_experts": main_res["hit_experts"],
         "roofline": roofline_for(main_res), "cpu_baseline": cpu, "also": also,
     }
