@@ -299,6 +299,30 @@ int moe_forward(const moe_problem* p, const void* x, const void* router_w,
                 const void* shared_gate, void* out, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Bytes of the fixed scratch array behind moe_forward_noalloc (64 MiB per
+ * GPU).  At the Qwen3-30B-A3B layer shape (H=2048, E=128, top-8, I=768) that
+ * holds the workspace of batches up to about a thousand tokens. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* The whole block without any allocation, for callers that cannot call
+ * hipMalloc or take a caller workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Same arguments, kernels
+ * and results (bit for bit) as moe_forward, but every intermediate lives in
+ * a fixed array of MOE_NOALLOC_SCRATCH_BYTES in device memory that the
+ * library holds on each GPU it runs on until the process ends.
+ *   - The current HIP device must be the one `stream` belongs to.  The
+ *     first call on a device looks up that device's copy of the array.
+ *   - A problem whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *     is rejected with MOE_ENOSPC before any HIP call.
+ *   - No hipMalloc, hipFree or other allocation happens in the call.
+ *   - Every call on one GPU shares the one array, which keeps the last
+ *     call's contents: calls that overlap on one GPU (several streams or
+ *     host threads at once) race and must be serialised by the caller. */
+int moe_forward_noalloc(const moe_problem* p, const void* x, const void* router_w,
+                        const void* w_gate_up, const void* w_down,
+                        const void* shared_w_gate_up, const void* shared_w_down,
+                        const void* shared_gate, void* out, void* stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -78,6 +78,7 @@ def load_library() -> ctypes.CDLL:
             "moe_shared_expert": [PP, _P, _P, _P, _P, _P, _P, _P],
             "moe_combine": [PP, _P, _P, _P, _P],
             "moe_forward": [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+            "moe_forward_noalloc": [PP, _P, _P, _P, _P, _P, _P, _P, _P, _P],
             "moe_dense_mlp": [PP, _P, _P, _P, _P, _P, _P],
             "moe_add_rmsnorm": [_I64, _I64, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_float, _P, _P],
             "moe_pack_weights": [_I64, _I64, _I64, ctypes.c_int32, _P, _P, _P],
@@ -602,4 +603,33 @@ def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob=True, shar
         _check(load_library().moe_forward(ctypes.byref(p), _ptr(x), _ptr(router_w), _ptr(w_gate_up), _ptr(w_down),
                                           _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(shared_gate),
                                           _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20     # the fixed scratch behind moe_forward_noalloc (include/moe_mi355x.h)
+
+
+def moe_forward_noalloc(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, shared_w_gate_up=None,
+                        shared_w_down=None, shared_gate=None, out=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
+    """The whole block through the allocation-free entry point: the library
+    keeps every intermediate in its fixed per-GPU scratch array (problems
+    whose workspace exceeds MOE_NOALLOC_SCRATCH_BYTES are rejected).  `out`
+    is allocated here only when not given."""
+    _check_forward_shapes(x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out)
+    p = problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up, weight_layout)
+    x = _gpu(x, "x")
+    dev = x.device
+    for t, n in ((router_w, "router_w"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
+        _gpu(t, n, x.dtype, dev)
+    for t, n in ((shared_w_gate_up, "shared_w_gate_up"), (shared_w_down, "shared_w_down"),
+                 (shared_gate, "shared_gate")):
+        if t is not None:
+            _gpu(t, n, x.dtype, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _gpu(out, "out", x.dtype, dev)
+    with torch.cuda.device(dev):
+        _check(load_library().moe_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(router_w), _ptr(w_gate_up),
+                                                  _ptr(w_down), _ptr(shared_w_gate_up), _ptr(shared_w_down),
+                                                  _ptr(shared_gate), _ptr(out), _stream(dev)))
     return out

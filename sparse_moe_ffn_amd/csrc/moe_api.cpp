@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moe_launch.h"
 #include "moe_mi355x.h"
@@ -459,27 +460,35 @@ int moe_combine(const moe_problem* p, const void* y, const void* shared_y, void*
                                         p->dtype, (hipStream_t)stream), "combine") ?: ok();
 }
 
-int moe_forward(const moe_problem* p, const void* x, const void* router_w, const void* w_gate_up,
-                const void* w_down, const void* shared_w_gate_up, const void* shared_w_down,
-                const void* shared_gate, void* out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the whole block, shared by moe_forward and
+// moe_forward_noalloc (everything but the workspace).  Returns MOE_OK, or an
+// error code with the message set; *empty is set when there is nothing to do.
+int check_forward(const moe_problem* p, const void* x, const void* router_w, const void* w_gate_up,
+                  const void* w_down, const void* shared_w_gate_up, const void* shared_w_down,
+                  const void* shared_gate, const void* out, bool* empty) {
+  *empty = false;
   if (int rc = check_problem(p)) return rc;
   const bool shared = shared_w_gate_up != nullptr;
   if (shared != (p->shared_inter > 0))
     return fail(MOE_EINVAL, "shared_w_gate_up must be given exactly when shared_inter > 0");
   if (shared && (!shared_w_down || !shared_gate)) return fail(MOE_EINVAL, "shared expert needs all three tensors");
-  if (p->num_tokens == 0) return ok();
-  if (!x || !router_w || !w_gate_up || !w_down || !out || !workspace) return fail(MOE_EINVAL, "NULL tensor");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(MOE_EUNSUPPORTED, "workspace must be 256-byte aligned");
-  moe_workspace_layout L;
-  layout_of(p, &L);
-  if (workspace_bytes < L.total_bytes)
-    return fail(MOE_ENOSPC, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total_bytes);
-  if (int rc = check_ptrs_bf16(p, {x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down,
-                                   shared_gate, out}))
-    return rc;
-  char* ws = static_cast<char*>(workspace);
+  if (p->num_tokens == 0) {
+    *empty = true;
+    return MOE_OK;
+  }
+  if (!x || !router_w || !w_gate_up || !w_down || !out) return fail(MOE_EINVAL, "NULL tensor");
+  return check_ptrs_bf16(p, {x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out});
+}
+
+// The launch sequence of the whole block over a workspace laid out as L.
+int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void* x, const void* router_w,
+                const void* w_gate_up, const void* w_down, const void* shared_w_gate_up,
+                const void* shared_w_down, const void* shared_gate, void* out, char* ws, void* stream) {
+  const bool shared = shared_w_gate_up != nullptr;
   auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
   int32_t* ids = (int32_t*)at(L.topk_ids);
   float* w = (float*)at(L.topk_w);
@@ -515,6 +524,85 @@ int moe_forward(const moe_problem* p, const void* x, const void* router_w, const
   }
   if (int rc = moe_combine(p, at(L.y), shared ? at(L.shared_y) : nullptr, out, stream)) return rc;
   return ok();
+}
+
+// ------------------------------------------------- allocation-free variant
+// The workspace of moe_forward_noalloc: one fixed array in device memory,
+// one copy per GPU the library runs on, held until the process ends.  In
+// host code `noalloc_scratch` names a host-side stand-in, not the device
+// copy: its device address comes from hipGetSymbolAddress, once per device,
+// and only that address is ever passed to a kernel.  Every call on one GPU
+// shares the array (the last call's contents stay in it); nothing in it has
+// to start at zero, because each call writes every region before reading
+// it.  Calls that overlap on one GPU (two streams, two host threads) race.
+static __device__ __align__(256) unsigned char noalloc_scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+// Device address of noalloc_scratch on the current device.
+int noalloc_scratch_ptr(char** ptr) {
+  int dev = -1;
+  if (int rc = hip_status(hipGetDevice(&dev), "hipGetDevice")) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EUNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* addr = nullptr;
+    if (int rc = hip_status(hipGetSymbolAddress(&addr, HIP_SYMBOL(noalloc_scratch)),
+                            "hipGetSymbolAddress(noalloc_scratch)"))
+      return rc;
+    if (!addr || (reinterpret_cast<uintptr_t>(addr) & 255u))
+      return fail(MOE_EHIP, "noalloc scratch has no usable device address");
+    g_noalloc_ptr[dev] = addr;
+  }
+  *ptr = static_cast<char*>(g_noalloc_ptr[dev]);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_problem* p, const void* x, const void* router_w, const void* w_gate_up,
+                const void* w_down, const void* shared_w_gate_up, const void* shared_w_down,
+                const void* shared_gate, void* out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  bool empty = false;
+  if (int rc = check_forward(p, x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out,
+                             &empty))
+    return rc;
+  if (empty) return ok();
+  if (!workspace) return fail(MOE_EINVAL, "NULL tensor");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MOE_EUNSUPPORTED, "workspace must be 256-byte aligned");
+  moe_workspace_layout L;
+  layout_of(p, &L);
+  if (workspace_bytes < L.total_bytes)
+    return fail(MOE_ENOSPC, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total_bytes);
+  return run_forward(p, L, x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out,
+                     static_cast<char*>(workspace), stream);
+}
+
+int moe_forward_noalloc(const moe_problem* p, const void* x, const void* router_w, const void* w_gate_up,
+                        const void* w_down, const void* shared_w_gate_up, const void* shared_w_down,
+                        const void* shared_gate, void* out, void* stream) {
+  bool empty = false;
+  if (int rc = check_forward(p, x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out,
+                             &empty))
+    return rc;
+  if (empty) return ok();
+  moe_workspace_layout L;
+  layout_of(p, &L);
+  if (L.total_bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ENOSPC,
+                "moe_forward_noalloc: this problem needs %zu bytes of scratch, more than its fixed %zu "
+                "(use moe_forward with a caller workspace)",
+                L.total_bytes, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  char* ws = nullptr;
+  if (int rc = noalloc_scratch_ptr(&ws)) return rc;
+  return run_forward(p, L, x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out, ws,
+                     stream);
 }
 
 }  // extern "C"

@@ -332,3 +332,29 @@ def test_shared_combine_dense_norm_reject_wrong_shapes():
     _expect(lambda: moe.moe_add_rmsnorm(x, _t(_N, _H + 64), w), "residual")
     _expect(lambda: moe.moe_add_rmsnorm(x, x, _t(_H + 8)), "weight")
     _expect(lambda: moe.moe_add_rmsnorm(x, x, w, normed=_t(_N + 1, _H)), "normed")
+
+
+def test_forward_noalloc_rejects_before_any_hip_call():
+    """The allocation-free entry point checks its arguments, and that the
+    problem fits its fixed scratch, before any HIP call (so on a machine
+    without a GPU too)."""
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    big = moe.problem(4096, 2048, 128, 8, 768)
+    assert moe.moe_workspace_size(big) > B.MOE_NOALLOC_SCRATCH_BYTES
+    rc = lib.moe_forward_noalloc(ctypes.byref(big), fake, fake, fake, fake, None, None, None, fake, None)
+    assert rc == B.MOE_ENOSPC and b"scratch" in lib.moe_last_error()
+    small = moe.problem(64, 2048, 128, 8, 768)
+    assert moe.moe_workspace_size(small) <= B.MOE_NOALLOC_SCRATCH_BYTES
+    rc = lib.moe_forward_noalloc(ctypes.byref(small), None, fake, fake, fake, None, None, None, fake, None)
+    assert rc == B.MOE_EINVAL
+    rc = lib.moe_forward_noalloc(ctypes.byref(small), fake, fake, fake, fake, fake, None, None, fake, None)
+    assert rc == B.MOE_EINVAL                               # shared weights without shared_inter
+    p0 = moe.problem(0, 64, 4, 2, 64)
+    assert lib.moe_forward_noalloc(ctypes.byref(p0), None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_SCRATCH_BYTES
