@@ -112,8 +112,16 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 constexpr int kRot = 13;   // K-start stride of every grouped product (see the launchers)
 
+// The grid may cover two problems of the same mode and tile shape (the routed
+// experts and the shared expert's dense rows): workgroups below blocks0 take
+// g0, the others g1; each workgroup's arithmetic is that of a launch of its
+// problem alone.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK, int ROT, bool SCAN>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g0, GemmProblem g1,
+                                                                                    int blocks0) {
+  const bool second = (int)blockIdx.x >= blocks0;
+  const GemmProblem& g = second ? g1 : g0;
+  const int bid = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(!BLK || BK == 64, "blocked weights come in 64-column blocks, one per stage");
   constexpr int kCpr = BK / 8;                      // 16-byte chunks per staged row
@@ -165,8 +173,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // that XCD's L2.
   const int m_tiles = grouped ? *g.num_tiles : (scan ? g.num_experts : (g.dense_rows + BM - 1) / BM);
   const int n_blocks = m_tiles * n_tiles_n;
-  if ((int)blockIdx.x >= n_blocks) return;
-  const int logical = xcd_swizzle(blockIdx.x, n_blocks);
+  if (bid >= n_blocks) return;
+  const int logical = xcd_swizzle(bid, n_blocks);
   const int mt = logical / n_tiles_n;
   const int nt = logical % n_tiles_n;
   int rows_valid, expert;
@@ -632,28 +640,41 @@ hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_
 // 32-, 64-, 128- and 320-row tiles (512 to 16384 tokens) within 1.2 us of
 // strides 7 and 5.
 // SCAN: the small-batch products that scan the top-k ids (16-row tiles).
+// g1 (optional, max_tiles 0 for none) must have the same mode, tile height
+// and weight layout as g0; its workgroups follow g0's, from a multiple of 8
+// (the XCD count) so each problem keeps its own XCD-aware tile order.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = kRot, bool SCAN = false>
-static hipError_t launch_bf16(const GemmProblem& g, hipStream_t s) {
-  if (g.block_m != BM) return hipErrorInvalidValue;   // tiles must be laid out for this height
-  const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
-  const int64_t blocks = (int64_t)g.max_tiles * n_tiles_n;
+static hipError_t launch_bf16(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s) {
+  if (g0.block_m != BM || (g1.max_tiles && g1.block_m != BM)) return hipErrorInvalidValue;
+  if (g1.max_tiles && g1.weights_blocked != g0.weights_blocked) return hipErrorInvalidValue;
+  auto blocks_of = [](const GemmProblem& g) {
+    const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
+    return (int64_t)g.max_tiles * n_tiles_n;
+  };
+  int64_t blocks0 = blocks_of(g0);
+  const int64_t blocks1 = g1.max_tiles ? blocks_of(g1) : 0;
+  if (blocks1) blocks0 = (blocks0 + 7) / 8 * 8;
+  const int64_t blocks = blocks0 + blocks1;
   if (blocks == 0) return hipSuccess;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64 * WAVES_M * WAVES_N);
-  if (g.weights_blocked)
+  if (g0.weights_blocked)
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, true, ROT, SCAN>),
-                       grid, block, 0, s, g);
+                       grid, block, 0, s, g0, g1, (int)blocks0);
   else
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<BM, BN, BK, WAVES_M, WAVES_N, SA, SB, MODE, false, ROT, SCAN>),
-                       grid, block, 0, s, g);
+                       grid, block, 0, s, g0, g1, (int)blocks0);
   return hipGetLastError();
 }
 
 template <int MODE>
-static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
+static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipStream_t s) {
   if (g.topk_ids && !g.sorted_pairs &&
       (g.dtype != MOE_BF16 || g.block_m != 16 || g.max_tiles != g.num_experts || g.num_pairs < 4 ||
        g.num_pairs > kScanMaxPairs || g.num_pairs % 4 != 0))
     return hipErrorInvalidValue;                       // outside what scan mode is built for
+  if (g1.max_tiles && (g.dtype != MOE_BF16 || g1.dtype != MOE_BF16 || g.topk_ids || g1.topk_ids))
+    return hipErrorInvalidValue;                       // pairs of problems: bf16 tiles only
   if (g.dtype == MOE_F32) {
     const dim3 grid(g.max_tiles, (g.n_out + kF32Cols - 1) / kF32Cols);
     if (grid.x == 0) return hipSuccess;
@@ -676,23 +697,31 @@ static hipError_t launch_mode(const GemmProblem& g, hipStream_t s) {
     //     60.0 with 8 waves.
     // Results are the same bit for bit: the tile width does not change any
     // row's arithmetic.
-    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, kRot, true>(g, s);
-    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, kRot, true>(g, s);
-    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, kRot, true>(g, s);
+    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, kRot, true>(g, g1, s);
+    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, kRot, true>(g, g1, s);
+    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, kRot, true>(g, g1, s);
   }
   switch (g.block_m) {
     case 16:   // small batches; down one weight slot shorter (75 -> 74 us)
-      if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, s);
-      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE>(g, s);
-    case 32: return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, s);
-    case 64: return launch_bf16<64, 256, 64, 1, 4, 2, 3, MODE>(g, s);
-    case 128: return launch_bf16<128, 256, 64, 2, 4, 2, 3, MODE>(g, s);
-    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE>(g, s);
+      if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
+      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE>(g, g1, s);
+    case 32: return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, g1, s);
+    case 64: return launch_bf16<64, 256, 64, 1, 4, 2, 3, MODE>(g, g1, s);
+    case 128: return launch_bf16<128, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);
+    case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE>(g, g1, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s) { return launch_mode<kGateUp>(g, s); }
-hipError_t launch_down(const GemmProblem& g, hipStream_t s) { return launch_mode<kDown>(g, s); }
+static const GemmProblem kNoProblem{};
+
+hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s) { return launch_mode<kGateUp>(g, kNoProblem, s); }
+hipError_t launch_down(const GemmProblem& g, hipStream_t s) { return launch_mode<kDown>(g, kNoProblem, s); }
+hipError_t launch_gate_up_pair(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s) {
+  return launch_mode<kGateUp>(g0, g1, s);
+}
+hipError_t launch_down_pair(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s) {
+  return launch_mode<kDown>(g0, g1, s);
+}
 
 }  // namespace moe

@@ -196,11 +196,11 @@ int check_ptrs_bf16(const moe_problem* p, std::initializer_list<const void*> ptr
   return MOE_OK;
 }
 
-// Dense SwiGLU over all rows of x: act = silu(x Wg^T) * (x Wu^T), then
-// c = scale[n] * (act Wd^T) (scale NULL: 1).
-int dense_swiglu(const moe_problem* p, int64_t inter, const void* x, const void* w_gate_up,
-                 const void* w_down, const float* scale, void* act, void* c, hipStream_t stream,
-                 const char* what_gate_up, const char* what_down) {
+// The two products of a dense SwiGLU over all rows of x:
+//   gate/up: act = silu(x Wg^T) * (x Wu^T);  down: c = scale[n] * (act Wd^T)
+// (scale NULL: 1).
+void dense_problems(const moe_problem* p, int64_t inter, const void* x, const void* w_gate_up, const void* w_down,
+                    const float* scale, void* act, void* c, moe::GemmProblem* gu, moe::GemmProblem* dn) {
   const int64_t N = p->num_tokens;
   const int64_t bm = dense_block_m(p);
   moe::GemmProblem g = gemm_common(p);
@@ -212,14 +212,65 @@ int dense_swiglu(const moe_problem* p, int64_t inter, const void* x, const void*
   g.c = act;
   g.K = (int32_t)p->hidden;
   g.n_out = (int32_t)inter;
-  if (int rc = hip_status(moe::launch_gate_up(g, stream), what_gate_up)) return rc;
+  *gu = g;
   g.a = act;
   g.b = w_down;
   g.c = c;
   g.scale = scale;
   g.K = (int32_t)inter;
   g.n_out = (int32_t)p->hidden;
-  return hip_status(moe::launch_down(g, stream), what_down);
+  *dn = g;
+}
+
+int dense_swiglu(const moe_problem* p, int64_t inter, const void* x, const void* w_gate_up,
+                 const void* w_down, const float* scale, void* act, void* c, hipStream_t stream,
+                 const char* what_gate_up, const char* what_down) {
+  moe::GemmProblem gu, dn;
+  dense_problems(p, inter, x, w_gate_up, w_down, scale, act, c, &gu, &dn);
+  if (int rc = hip_status(moe::launch_gate_up(gu, stream), what_gate_up)) return rc;
+  return hip_status(moe::launch_down(dn, stream), what_down);
+}
+
+// The grouped products over an align table.
+moe::GemmProblem grouped_gate_up_problem(const moe_problem* p, const void* x, const void* w_gate_up,
+                                         const int32_t* sorted_pairs, const int32_t* tile_expert,
+                                         const int32_t* tile_rows, const int32_t* num_tiles, int64_t block_m,
+                                         int64_t max_tiles, void* act) {
+  moe::GemmProblem g = gemm_common(p);
+  g.a = x;
+  g.b = w_gate_up;
+  g.sorted_pairs = sorted_pairs;
+  g.tile_expert = tile_expert;
+  g.tile_rows = tile_rows;
+  g.num_tiles = num_tiles;
+  g.c = act;
+  g.expert_stride = 2 * p->inter * p->hidden;
+  g.K = (int32_t)p->hidden;
+  g.n_out = (int32_t)p->inter;
+  g.block_m = (int32_t)block_m;
+  g.max_tiles = (int32_t)max_tiles;
+  return g;
+}
+
+moe::GemmProblem grouped_down_problem(const moe_problem* p, const void* act, const void* w_down, const float* topk_w,
+                                      const int32_t* sorted_pairs, const int32_t* tile_expert,
+                                      const int32_t* tile_rows, const int32_t* num_tiles, int64_t block_m,
+                                      int64_t max_tiles, void* y) {
+  moe::GemmProblem g = gemm_common(p);
+  g.a = act;
+  g.b = w_down;
+  g.sorted_pairs = sorted_pairs;
+  g.tile_expert = tile_expert;
+  g.tile_rows = tile_rows;
+  g.num_tiles = num_tiles;
+  g.scale = topk_w;
+  g.c = y;
+  g.expert_stride = p->hidden * p->inter;
+  g.K = (int32_t)p->inter;
+  g.n_out = (int32_t)p->hidden;
+  g.block_m = (int32_t)block_m;
+  g.max_tiles = (int32_t)max_tiles;
+  return g;
 }
 
 }  // namespace
@@ -327,19 +378,8 @@ int moe_gate_up(const moe_problem* p, const void* x, const void* w_gate_up, cons
   if (!block_m_supported(p->dtype, block_m)) return fail(MOE_EUNSUPPORTED, "block_m %lld", (long long)block_m);
   if (max_tiles < 0 || max_tiles >= ((int64_t)1 << 24)) return fail(MOE_EINVAL, "bad max_tiles");
   if (int rc = check_ptrs_bf16(p, {x, w_gate_up, act})) return rc;
-  moe::GemmProblem g = gemm_common(p);
-  g.a = x;
-  g.b = w_gate_up;
-  g.sorted_pairs = sorted_pairs;
-  g.tile_expert = tile_expert;
-  g.tile_rows = tile_rows;
-  g.num_tiles = num_tiles;
-  g.c = act;
-  g.expert_stride = 2 * p->inter * p->hidden;
-  g.K = (int32_t)p->hidden;
-  g.n_out = (int32_t)p->inter;
-  g.block_m = (int32_t)block_m;
-  g.max_tiles = (int32_t)max_tiles;
+  const moe::GemmProblem g = grouped_gate_up_problem(p, x, w_gate_up, sorted_pairs, tile_expert, tile_rows,
+                                                     num_tiles, block_m, max_tiles, act);
   return hip_status(moe::launch_gate_up(g, (hipStream_t)stream), "gate_up") ?: ok();
 }
 
@@ -353,20 +393,8 @@ int moe_down(const moe_problem* p, const void* act, const void* w_down, const fl
   if (!block_m_supported(p->dtype, block_m)) return fail(MOE_EUNSUPPORTED, "block_m %lld", (long long)block_m);
   if (max_tiles < 0 || max_tiles >= ((int64_t)1 << 24)) return fail(MOE_EINVAL, "bad max_tiles");
   if (int rc = check_ptrs_bf16(p, {act, w_down, y})) return rc;
-  moe::GemmProblem g = gemm_common(p);
-  g.a = act;
-  g.b = w_down;
-  g.sorted_pairs = sorted_pairs;
-  g.tile_expert = tile_expert;
-  g.tile_rows = tile_rows;
-  g.num_tiles = num_tiles;
-  g.scale = topk_w;
-  g.c = y;
-  g.expert_stride = p->hidden * p->inter;
-  g.K = (int32_t)p->inter;
-  g.n_out = (int32_t)p->hidden;
-  g.block_m = (int32_t)block_m;
-  g.max_tiles = (int32_t)max_tiles;
+  const moe::GemmProblem g = grouped_down_problem(p, act, w_down, topk_w, sorted_pairs, tile_expert, tile_rows,
+                                                  num_tiles, block_m, max_tiles, y);
   return hip_status(moe::launch_down(g, (hipStream_t)stream), "down") ?: ok();
 }
 
@@ -489,6 +517,9 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
                 const void* w_gate_up, const void* w_down, const void* shared_w_gate_up,
                 const void* shared_w_down, const void* shared_gate, void* out, char* ws, void* stream) {
   const bool shared = shared_w_gate_up != nullptr;
+  // The shared expert joins the routed products' launches when both run the
+  // same bf16 tile height.
+  const bool merge_shared = shared && !L.ids_products && p->dtype == MOE_BF16 && dense_block_m(p) == L.block_m;
   auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
   int32_t* ids = (int32_t*)at(L.topk_ids);
   float* w = (float*)at(L.topk_w);
@@ -510,14 +541,31 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
                            (int32_t*)at(L.offsets), (int32_t*)at(L.order), sorted, texp, trows, ntiles,
                            (int32_t*)at(L.align_scratch), stream))
       return rc;
-    if (int rc = moe_gate_up(p, x, w_gate_up, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
-                             at(L.act), stream))
-      return rc;
-    if (int rc = moe_down(p, at(L.act), w_down, w, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
-                          at(L.y), stream))
-      return rc;
+    if (merge_shared) {
+      // One gate/up and one down launch cover the routed tiles and the shared
+      // expert's dense tiles (same tile height): one ramp-up and one tail per
+      // product instead of two, and the small shared launches no longer run
+      // a partial round of workgroups on their own.
+      moe::GemmProblem sgu, sdn;
+      dense_problems(p, p->shared_inter, x, shared_w_gate_up, shared_w_down, sscale, at(L.shared_act),
+                     at(L.shared_y), &sgu, &sdn);
+      const moe::GemmProblem gu = grouped_gate_up_problem(p, x, w_gate_up, sorted, texp, trows, ntiles, L.block_m,
+                                                          L.max_tiles, at(L.act));
+      if (int rc = hip_status(moe::launch_gate_up_pair(gu, sgu, (hipStream_t)stream), "gate_up with shared"))
+        return rc;
+      const moe::GemmProblem dn = grouped_down_problem(p, at(L.act), w_down, w, sorted, texp, trows, ntiles,
+                                                       L.block_m, L.max_tiles, at(L.y));
+      if (int rc = hip_status(moe::launch_down_pair(dn, sdn, (hipStream_t)stream), "down with shared")) return rc;
+    } else {
+      if (int rc = moe_gate_up(p, x, w_gate_up, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
+                               at(L.act), stream))
+        return rc;
+      if (int rc = moe_down(p, at(L.act), w_down, w, sorted, texp, trows, ntiles, L.block_m, L.max_tiles,
+                            at(L.y), stream))
+        return rc;
+    }
   }
-  if (shared) {
+  if (shared && !merge_shared) {
     if (int rc = moe_shared_expert(p, x, shared_w_gate_up, shared_w_down, sscale, at(L.shared_act),
                                    at(L.shared_y), stream))
       return rc;

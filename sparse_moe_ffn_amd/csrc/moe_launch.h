@@ -59,6 +59,10 @@ constexpr int kScanMaxPairs = 1024;   // ids that fit the 16-row tile's A ring (
 
 hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s);
 hipError_t launch_down(const GemmProblem& g, hipStream_t s);
+// Two problems in one launch (bf16, same tile height and weight layout, no
+// scan mode): the routed experts' tiles, then the shared expert's dense rows.
+hipError_t launch_gate_up_pair(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s);
+hipError_t launch_down_pair(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s);
 
 // Row-major bf16 [batch, rows, cols] -> the blocked layout (rows % 8 == 0,
 // cols % 64 == 0).

@@ -391,3 +391,35 @@ def test_forward_multichunk_grouping_equals_staged(N, H, E, k, I, Is):
     ref = moe.moe_combine(y, N, k, sy)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("N,H,E,k,I,Is", [(4100, 128, 8, 2, 64, 192), (200, 128, 16, 4, 192, 128),
+                                          (1300, 256, 32, 8, 128, 64), (8192, 256, 128, 8, 128, 256),
+                                          (700, 192, 300, 8, 64, 192)])
+def test_forward_with_shared_equals_staged(N, H, E, k, I, Is):
+    """moe_forward runs the shared expert's products in the routed products'
+    launches when both take the same tile height (all but the last case
+    here); the output must equal the staged public calls bit for bit."""
+    cfg = random_case(N, H, E, k, I, I_shared=Is, dtype="bf16", seed=23)
+    t = make_inputs(cfg, DEV)
+    for layout in (moe.MOE_LAYOUT_ROW_MAJOR, moe.MOE_LAYOUT_BLOCKED):
+        tw = dict(t)
+        if layout == moe.MOE_LAYOUT_BLOCKED:
+            for name in ("w_gate_up", "w_down", "shared_w_gate_up", "shared_w_down"):
+                tw[name] = moe.moe_pack_weights(t[name])
+        out = moe.moe_forward(tw["x"], tw["router_w"], tw["w_gate_up"], tw["w_down"], k, cfg.norm_topk_prob,
+                              tw["shared_w_gate_up"], tw["shared_w_down"], tw["shared_gate"], weight_layout=layout)
+        lay = moe.moe_get_workspace_layout(moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], k,
+                                                            cfg.norm_topk_prob, t["shared_w_gate_up"]))
+        ids, w, sc = moe.moe_route(t["x"], t["router_w"], k, cfg.norm_topk_prob, t["shared_gate"])
+        if lay["ids_products"]:
+            act = moe.moe_gate_up_ids(t["x"], tw["w_gate_up"], ids, weight_layout=layout)
+            y = moe.moe_down_ids(act, tw["w_down"], ids, w, weight_layout=layout)
+        else:
+            gr = moe.moe_align(ids, E, lay["block_m"])
+            act = moe.moe_gate_up(t["x"], tw["w_gate_up"], gr, k, weight_layout=layout)
+            y = moe.moe_down(act, tw["w_down"], w, gr, N, k, weight_layout=layout)
+        _, sy = moe.moe_shared_expert(t["x"], tw["shared_w_gate_up"], tw["shared_w_down"], sc, weight_layout=layout)
+        ref = moe.moe_combine(y, N, k, sy)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"layout {layout}: moe_forward differs from the staged calls"
