@@ -33,6 +33,7 @@ constexpr int kLogitsThreads = 256;           // 4 waves
 constexpr int kLogitsWaves = kLogitsThreads / kWave;
 constexpr int kMaxSubPerWave = 9;             // 16-column sub-tiles per wave: 4*9*16 >= 512+1
 constexpr int kSelectWaves = 4;               // tokens per select workgroup
+constexpr int kRoundsMaxK = 8;                // top-k by argmax rounds up to this k, radix select above
 
 // Columns of the partial tiles: E router rows, the shared gate, padding to 16.
 __host__ __device__ constexpr int route_cols(int E, bool shared) { return ((E + (shared ? 1 : 0) + 15) / 16) * 16; }
@@ -163,6 +164,65 @@ __device__ __forceinline__ void route_token(const float (&lg)[PER], int E, int k
   wave_lds_fence();
 }
 
+// The same selection as route_token for small k, as k rounds of a wave-wide
+// argmax: each round takes the largest remaining probability, the lowest
+// expert id among equal ones (the lowest block of 64 ids with a match, then
+// its lowest lane), and removes it.  Rounds come out in descending order with
+// ties to the lower id, so slot j is round j; the renormalising sum adds the
+// rounds in order, as route_token adds the slots.  Same ids, weights and
+// slot order, in fewer dependent steps than the radix select when k is small.
+template <int PER>
+__device__ __forceinline__ void route_token_rounds(const float (&lg)[PER], int E, int k, int norm,
+                                                   int32_t* __restrict__ ids_out, float* __restrict__ w_out) {
+  const int lane = lane_id();
+  float m = -FLT_MAX;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + kWave * i < E) m = fmaxf(m, lg[i]);
+  m = wave_reduce_dpp(m, -FLT_MAX, [](float a, float b) { return fmaxf(a, b); });
+  float z[PER];
+  float zs = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    z[i] = (lane + kWave * i < E) ? expf(lg[i] - m) : 0.0f;
+    zs += z[i];
+  }
+  const float s = wave_reduce_dpp(zs, 0.0f, [](float a, float b) { return a + b; });
+  float v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool in = lane + kWave * i < E;
+    const float pr = in ? z[i] / s : 0.0f;
+    v[i] = in ? ((pr == pr) ? pr : 0.0f) : -1.0f;     // -1: no expert here
+  }
+  int my_id = 0;
+  float my_v = 0.0f, t = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float lm = v[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) lm = fmaxf(lm, v[i]);
+    const float M = wave_reduce_dpp(lm, -FLT_MAX, [](float a, float b) { return fmaxf(a, b); });
+    int id = 0;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {               // the lowest block with a match wins
+      const unsigned long long b = __ballot(v[i] == M);
+      if (b) id = kWave * i + (int)__builtin_ctzll(b);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane + kWave * i == id) v[i] = -1.0f;
+    if (lane == j) {
+      my_id = id;
+      my_v = M;
+    }
+    t += M;                                            // slot order
+  }
+  if (lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = norm ? my_v / t : my_v;
+  }
+}
+
 template <int PER>
 __global__ __launch_bounds__(kSelectWaves * kWave) void route_select_kernel(
     const float* __restrict__ partial, int N, int E, int k, int norm, int has_shared, int cols,
@@ -195,8 +255,11 @@ __global__ __launch_bounds__(kSelectWaves * kWave) void route_select_kernel(
     for (int sl = 0; sl < kSlices; ++sl) acc += src[sl * slice + E];
     shared_scale[n] = sigmoid_f32(acc);
   }
-  route_token<PER>(lg, E, k, norm, sel_v[wave], sel_e[wave], sel_o[wave], ids + (int64_t)n * k,
-                   w + (int64_t)n * k);
+  if (k <= kRoundsMaxK)
+    route_token_rounds<PER>(lg, E, k, norm, ids + (int64_t)n * k, w + (int64_t)n * k);
+  else
+    route_token<PER>(lg, E, k, norm, sel_v[wave], sel_e[wave], sel_o[wave], ids + (int64_t)n * k,
+                     w + (int64_t)n * k);
 }
 
 // ------------------------------------------------------------- logits
