@@ -8,11 +8,14 @@
 // (lshu.cn/news/442807), qwen3_moe.py, Qwen3MoeSparseMoeBlock forward.
 //
 // Two kernels:
-//   logits: a (16-token tile) x (H slice) grid.  Each workgroup multiplies
-//     16 tokens by every router row over one of kSlices slices of H
-//     (16x16x32 bf16 MFMA, float32 accumulation; fp32: plain FMA) and writes
-//     a partial logit tile.  Spreading H over workgroups spreads the router
-//     weight reads over many CUs, which is what matters for small batches.
+//   logits: a (token tile) x (H slice) grid.  Each workgroup multiplies its
+//     tokens by router rows over one of kSlices slices of H (16x16x32 bf16
+//     MFMA, float32 accumulation; fp32: plain FMA) and writes a partial
+//     logit tile.  Spreading H over workgroups spreads the router weight
+//     reads over many CUs, which is what matters for small batches; there a
+//     workgroup is a single wave for 16 tokens and three 16-column
+//     sub-tiles, so a 64-token batch runs on 96 CUs.  Large batches take
+//     64-token tiles and every column, so the router rows are re-read less.
 //   select: one wave per token.  The kSlices partials are summed in slice
 //     order (the same order for every batch size, so a token's routing does
 //     not depend on the batch), then softmax, top-k and renormalisation run
@@ -32,6 +35,9 @@ constexpr int kSlices = 8;                    // H slices (fixed for every N)
 constexpr int kLogitsThreads = 256;           // 4 waves
 constexpr int kLogitsWaves = kLogitsThreads / kWave;
 constexpr int kMaxSubPerWave = 9;             // 16-column sub-tiles per wave: 4*9*16 >= 512+1
+constexpr int kSmallSub = 3;                  // 16-column sub-tiles of a small-batch logits wave
+constexpr int kLargeTiles = 4;                // 16-token tiles of a large-batch logits workgroup
+constexpr int kLargeBatch = 512;              // tokens from which the large-batch tiling is used
 constexpr int kSelectWaves = 4;               // tokens per select workgroup
 constexpr int kRoundsMaxK = 8;                // top-k by argmax rounds up to this k, radix select above
 
@@ -263,17 +269,95 @@ __global__ __launch_bounds__(kSelectWaves * kWave) void route_select_kernel(
 }
 
 // ------------------------------------------------------------- logits
-// Partial logits of 16*TT tokens over H slice blockIdx.y:
+// Partial logits over H slice blockIdx.y:
 //   partial[slice][n][c] = sum_{h in slice} x[n, h] * row_c[h],
 // row_c = router_w[c] for c < E, the shared gate for c == E, zero beyond.
-// Wave w owns column sub-tiles w, w+4, ... (at most SUBW) and all TT row
-// tiles, so one router fragment feeds TT matrix instructions; a lane holds 4
-// rows of one column of each 16x16 sub-tile.  Small batches use TT = 1 (more
-// workgroups share the router reads), large ones TT = 4 (fewer re-reads).
-template <int TT, int SUBW>
+// Every logit is one chain of matrix instructions over the slice's 32-wide
+// k-steps in increasing order, from a zero accumulator, whichever kernel
+// and tile computes it, so both tilings give the same bits.  A lane holds 4
+// rows of one column of each 16x16 sub-tile.
+
+// Column c's router row, offset to this lane's 8-element piece, or null.
+__device__ __forceinline__ const uint16_t* router_row(const uint16_t* router_w, const uint16_t* shared_gate, int c,
+                                                      int E, int H, int lane) {
+  const uint16_t* src = nullptr;
+  if (c < E) src = router_w + (int64_t)c * H;
+  else if (c == E && shared_gate) src = shared_gate;
+  return src ? src + (lane >> 4) * 8 : nullptr;
+}
+
+// Small batches: one wave per workgroup, for 16 tokens (blockIdx.x), one H
+// slice (blockIdx.y) and kSmallSub column sub-tiles (blockIdx.z).  Many
+// small workgroups put the router reads of a small batch on many CUs at
+// once; each wave loads its own x fragments (the same 16 rows for every
+// sub-tile group, from L2).
+__global__ __launch_bounds__(kWave) void route_logits_small_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ router_w, const uint16_t* __restrict__ shared_gate,
+    int N, int H, int E, int cols, float* __restrict__ partial) {
+  const int lane = lane_id();
+  const int t0 = blockIdx.x * kRouteTok;
+  const int sub0 = blockIdx.z * kSmallSub;
+  const int nsub = cols / 16;
+  const int ksteps = H / 32;
+  const int per_slice = (ksteps + kSlices - 1) / kSlices;
+  const int kb = blockIdx.y * per_slice, ke = min(ksteps, kb + per_slice);
+  const uint16_t* a_src = x + (int64_t)min(t0 + (lane & 15), N - 1) * H + (lane >> 4) * 8;
+  const uint16_t* b_src[kSmallSub];
+  floatx4 acc[kSmallSub];
+#pragma unroll
+  for (int i = 0; i < kSmallSub; ++i) {
+    b_src[i] = (sub0 + i < nsub) ? router_row(router_w, shared_gate, (sub0 + i) * 16 + (lane & 15), E, H, lane)
+                                 : nullptr;
+    acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint4 zero = {0u, 0u, 0u, 0u};
+  constexpr int kUnroll = 8;                           // one round per slice at H = 2048
+  for (int s0 = kb; s0 < ke; s0 += kUnroll) {
+    uint4 a[kUnroll];
+    uint4 b[kUnroll][kSmallSub];
+    // Steps past the slice end reload its last step (in bounds, never used).
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k0 = min(s0 + u, ke - 1) * 32;
+      a[u] = *reinterpret_cast<const uint4*>(a_src + k0);
+#pragma unroll
+      for (int i = 0; i < kSmallSub; ++i) b[u][i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (s0 + u < ke) {
+#pragma unroll
+        for (int i = 0; i < kSmallSub; ++i) acc[i] = mfma16x16x32(a[u], b[u][i], acc[i]);
+      }
+  }
+  float* dst = partial + (int64_t)blockIdx.y * N * cols;
+#pragma unroll
+  for (int i = 0; i < kSmallSub; ++i) {
+    if (sub0 + i < nsub) {
+      const int c = (sub0 + i) * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = t0 + (lane >> 4) * 4 + r;
+        if (n < N) dst[(int64_t)n * cols + c] = acc[i][r];
+      }
+    }
+  }
+}
+
+// Large batches: kLargeTiles 16-token tiles (blockIdx.x) and one H slice
+// (blockIdx.y) per 4-wave workgroup.  Wave w owns column sub-tiles w, w+4,
+// ... (at most SUBW) and all token tiles, so one router fragment feeds
+// kLargeTiles matrix instructions.  Wave w < kLargeTiles loads the x
+// fragments of tile w for a chunk of k-steps into LDS (in fragment order:
+// lane-linear 1 KB blocks, so the reads are conflict-free), and every wave
+// multiplies all tiles with its router fragments: each x fragment is loaded
+// from memory once per workgroup instead of once per wave.
+template <int SUBW>
 __global__ __launch_bounds__(kLogitsThreads) void route_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ router_w, const uint16_t* __restrict__ shared_gate,
     int N, int H, int E, int cols, float* __restrict__ partial) {
+  constexpr int TT = kLargeTiles;
+  static_assert(TT <= kLogitsWaves, "one loading wave per token tile");
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int t0 = blockIdx.x * kRouteTok * TT;
@@ -282,97 +366,49 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_bf16_kernel(
   const int per_slice = (ksteps + kSlices - 1) / kSlices;
   const int kb = blockIdx.y * per_slice, ke = min(ksteps, kb + per_slice);
 
-  const uint16_t* a_src[TT];
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int arow = min(t0 + t * 16 + (lane & 15), N - 1);
-    a_src[t] = x + (int64_t)arow * H + (lane >> 4) * 8;
-  }
   const uint16_t* b_src[SUBW];
   floatx4 acc[TT][SUBW];
 #pragma unroll
   for (int i = 0; i < SUBW; ++i) {
-    const int c = (wave + kLogitsWaves * i) * 16 + (lane & 15);
-    const uint16_t* src = nullptr;
-    if (c < E) src = router_w + (int64_t)c * H;
-    else if (c == E && shared_gate) src = shared_gate;
-    b_src[i] = src ? src + (lane >> 4) * 8 : nullptr;
+    b_src[i] = router_row(router_w, shared_gate, (wave + kLogitsWaves * i) * 16 + (lane & 15), E, H, lane);
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t][i] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const uint4 zero = {0u, 0u, 0u, 0u};
-  if constexpr (TT == 1) {
-    constexpr int kUnroll = 4;
-    for (int s0 = kb; s0 < ke; s0 += kUnroll) {
-      uint4 a[kUnroll][TT];
-      uint4 b[kUnroll][SUBW];
+  constexpr int kChunk = (SUBW <= 3) ? 8 : 2;         // k-steps per LDS round (register budget)
+  __shared__ uint4 a_lds[TT][kChunk][kWave];
+  const uint16_t* my_a = x + (int64_t)min(t0 + wave * 16 + (lane & 15), N - 1) * H + (lane >> 4) * 8;
+  for (int s0 = kb; s0 < ke; s0 += kChunk) {
+    const int ns = min(kChunk, ke - s0);
+    // Steps past the slice end reload its last step (in bounds, never used).
+    if (wave < TT) {
+      uint4 a[kChunk];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (s0 + u < ke) {
-          const int k0 = (s0 + u) * 32;
+      for (int u = 0; u < kChunk; ++u) a[u] = *reinterpret_cast<const uint4*>(my_a + min(s0 + u, ke - 1) * 32);
 #pragma unroll
-          for (int t = 0; t < TT; ++t) a[u][t] = *reinterpret_cast<const uint4*>(a_src[t] + k0);
+      for (int u = 0; u < kChunk; ++u) a_lds[wave][u][lane] = a[u];
+    }
+    uint4 b[kChunk][SUBW];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int k0 = min(s0 + u, ke - 1) * 32;
+#pragma unroll
+      for (int i = 0; i < SUBW; ++i) b[u][i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if (u < ns) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const uint4 af = a_lds[t][u][lane];
 #pragma unroll
           for (int i = 0; i < SUBW; ++i)
-            if (wave + kLogitsWaves * i < nsub)
-              b[u][i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (s0 + u < ke) {
-#pragma unroll
-          for (int i = 0; i < SUBW; ++i)
-            if (wave + kLogitsWaves * i < nsub) {
-#pragma unroll
-              for (int t = 0; t < TT; ++t) acc[t][i] = mfma16x16x32(a[u][t], b[u][i], acc[t][i]);
-            }
+            if (wave + kLogitsWaves * i < nsub) acc[t][i] = mfma16x16x32(af, b[u][i], acc[t][i]);
         }
       }
     }
-  } else {
-    // TT token tiles: wave w < TT loads the fragments of tile w for a chunk
-    // of k-steps into LDS (in fragment order: lane-linear 1 KB blocks, so the
-    // reads are conflict-free), and every wave multiplies all TT tiles with
-    // its router fragments.  Each x fragment is loaded from memory once per
-    // workgroup instead of once per wave.  The k-steps are still taken in
-    // order, so every logit is summed exactly as in the TT = 1 path.
-    static_assert(TT <= kLogitsWaves, "one loading wave per token tile");
-    constexpr int kChunk = (SUBW <= 3) ? 8 : 2;       // k-steps per LDS round (register budget)
-    __shared__ uint4 a_lds[TT][kChunk][kWave];
-    const uint16_t* my_a = x + (int64_t)min(t0 + wave * 16 + (lane & 15), N - 1) * H + (lane >> 4) * 8;
-    for (int s0 = kb; s0 < ke; s0 += kChunk) {
-      const int ns = min(kChunk, ke - s0);
-      // Steps past the slice end reload its last step (in bounds, never used).
-      if (wave < TT) {
-        uint4 a[kChunk];
-#pragma unroll
-        for (int u = 0; u < kChunk; ++u) a[u] = *reinterpret_cast<const uint4*>(my_a + min(s0 + u, ke - 1) * 32);
-#pragma unroll
-        for (int u = 0; u < kChunk; ++u) a_lds[wave][u][lane] = a[u];
-      }
-      uint4 b[kChunk][SUBW];
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        const int k0 = min(s0 + u, ke - 1) * 32;
-#pragma unroll
-        for (int i = 0; i < SUBW; ++i) b[u][i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : zero;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        if (u < ns) {
-#pragma unroll
-          for (int t = 0; t < TT; ++t) {
-            const uint4 af = a_lds[t][u][lane];
-#pragma unroll
-            for (int i = 0; i < SUBW; ++i)
-              if (wave + kLogitsWaves * i < nsub) acc[t][i] = mfma16x16x32(af, b[u][i], acc[t][i]);
-          }
-        }
-      }
-      __syncthreads();
-    }
+    __syncthreads();
   }
   float* dst = partial + (int64_t)blockIdx.y * N * cols;
 #pragma unroll
@@ -424,20 +460,19 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* router_
   const bool shared = shared_gate != nullptr;
   const int cols = route_cols(E, shared);
   if (p.dtype == MOE_BF16) {
-    auto go_logits = [&](auto tt, auto subw) {
-      constexpr int TT = decltype(tt)::value, SUBW = decltype(subw)::value;
-      const dim3 lgrid((N + kRouteTok * TT - 1) / (kRouteTok * TT), kSlices);
-      hipLaunchKernelGGL((route_logits_bf16_kernel<TT, SUBW>), lgrid, dim3(kLogitsThreads), 0, s,
-                         (const uint16_t*)x, (const uint16_t*)router_w, (const uint16_t*)shared_gate, N, H, E, cols,
-                         scratch);
-    };
-    const bool narrow = cols <= 16 * kLogitsWaves * 3;
-    if (N >= 512) {
-      if (narrow) go_logits(std::integral_constant<int, 4>{}, std::integral_constant<int, 3>{});
-      else go_logits(std::integral_constant<int, 4>{}, std::integral_constant<int, kMaxSubPerWave>{});
+    const uint16_t *xb = (const uint16_t*)x, *rb = (const uint16_t*)router_w, *gb = (const uint16_t*)shared_gate;
+    const int nsub = cols / 16;
+    if (N >= kLargeBatch) {
+      const dim3 lgrid((N + kRouteTok * kLargeTiles - 1) / (kRouteTok * kLargeTiles), kSlices);
+      if (cols <= 16 * kLogitsWaves * 3)
+        hipLaunchKernelGGL((route_logits_bf16_kernel<3>), lgrid, dim3(kLogitsThreads), 0, s, xb, rb, gb, N, H, E, cols,
+                           scratch);
+      else
+        hipLaunchKernelGGL((route_logits_bf16_kernel<kMaxSubPerWave>), lgrid, dim3(kLogitsThreads), 0, s, xb, rb, gb, N,
+                           H, E, cols, scratch);
     } else {
-      if (narrow) go_logits(std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{});
-      else go_logits(std::integral_constant<int, 1>{}, std::integral_constant<int, kMaxSubPerWave>{});
+      const dim3 lgrid((N + kRouteTok - 1) / kRouteTok, kSlices, (nsub + kSmallSub - 1) / kSmallSub);
+      hipLaunchKernelGGL(route_logits_small_bf16_kernel, lgrid, dim3(kWave), 0, s, xb, rb, gb, N, H, E, cols, scratch);
     }
   } else {
     const dim3 lgrid((N + kRouteTok - 1) / kRouteTok, kSlices);
