@@ -38,6 +38,7 @@ constexpr int kMaxSubPerWave = 9;             // 16-column sub-tiles per wave: 4
 constexpr int kSmallSub = 3;                  // 16-column sub-tiles of a small-batch logits wave
 constexpr int kLargeTiles = 4;                // 16-token tiles of a large-batch logits workgroup
 constexpr int kLargeBatch = 512;              // tokens from which the large-batch tiling is used
+constexpr int kXcds = 8;                      // XCDs of the GPU; workgroups are dealt to them in turn
 constexpr int kSelectWaves = 4;               // tokens per select workgroup
 constexpr int kRoundsMaxK = 8;                // top-k by argmax rounds up to this k, radix select above
 
@@ -229,16 +230,28 @@ __device__ __forceinline__ void route_token_rounds(const float (&lg)[PER], int E
   }
 }
 
+// One wave per token, kSelectWaves tokens per workgroup.  After the
+// large-batch logits kernel (by_tile set), workgroup b takes its tokens from
+// a tile that was written on its own XCD (b % 8): tile b % 8 + 8 g, g =
+// (b / 8) / kSelectPerTile, so the partials are read from that XCD's L2.
+constexpr int kSelectPerTile = kRouteTok * kLargeTiles / kSelectWaves;   // select workgroups per large tile
+
 template <int PER>
 __global__ __launch_bounds__(kSelectWaves * kWave) void route_select_kernel(
-    const float* __restrict__ partial, int N, int E, int k, int norm, int has_shared, int cols,
+    const float* __restrict__ partial, int N, int E, int k, int norm, int has_shared, int cols, int by_tile,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ shared_scale) {
   __shared__ float sel_v[kSelectWaves][kMaxTopK];
   __shared__ int sel_e[kSelectWaves][kMaxTopK];
   __shared__ float sel_o[kSelectWaves][kMaxTopK];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int n = blockIdx.x * kSelectWaves + wave;
+  int first = blockIdx.x * kSelectWaves;
+  if (by_tile) {
+    const int b = blockIdx.x, q = b / kXcds;
+    const int tile = b % kXcds + kXcds * (q / kSelectPerTile);
+    first = tile * kRouteTok * kLargeTiles + (q % kSelectPerTile) * kSelectWaves;
+  }
+  const int n = first + wave;
   if (n >= N) return;                                      // whole wave leaves together
   const int64_t slice = (int64_t)N * cols;
   const float* src = partial + (int64_t)n * cols;
@@ -344,27 +357,42 @@ __global__ __launch_bounds__(kWave) void route_logits_small_bf16_kernel(
   }
 }
 
-// Large batches: kLargeTiles 16-token tiles (blockIdx.x) and one H slice
-// (blockIdx.y) per 4-wave workgroup.  Wave w owns column sub-tiles w, w+4,
-// ... (at most SUBW) and all token tiles, so one router fragment feeds
-// kLargeTiles matrix instructions.  Wave w < kLargeTiles loads the x
-// fragments of tile w for a chunk of k-steps into LDS (in fragment order:
-// lane-linear 1 KB blocks, so the reads are conflict-free), and every wave
-// multiplies all tiles with its router fragments: each x fragment is loaded
-// from memory once per workgroup instead of once per wave.
+// Large batches: one 4-wave workgroup per (tile of kLargeTiles 16-token
+// tiles, H slice).  Wave w owns column sub-tiles w, w+4, ... (at most SUBW)
+// and all token tiles, so one router fragment feeds kLargeTiles matrix
+// instructions.  Wave w < kLargeTiles loads the x fragments of tile w for a
+// chunk of k-steps into LDS (in fragment order: lane-linear 1 KB blocks, so
+// the reads are conflict-free), and every wave multiplies all tiles with its
+// router fragments: each x fragment is loaded from memory once per
+// workgroup instead of once per wave.
+//
+// Placement: workgroups are dealt to the 8 XCDs in turn by linear id, and
+// linear id L takes tile 8 (L / 64) + L % 8 and slice (L / 8) % 8.  So all
+// slices of tile t are written from XCD t % 8, groups of 8 tiles are
+// dispatched one after the other, and the select kernel (which reads tile
+// t's partials from XCD t % 8) finds them in that XCD's L2.  The grid holds
+// whole groups; workgroups past the last tile leave at once.
+__host__ __device__ constexpr int large_tile_groups(int N) {
+  return ((N + kRouteTok * kLargeTiles - 1) / (kRouteTok * kLargeTiles) + kXcds - 1) / kXcds;
+}
+
 template <int SUBW>
 __global__ __launch_bounds__(kLogitsThreads) void route_logits_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ router_w, const uint16_t* __restrict__ shared_gate,
     int N, int H, int E, int cols, float* __restrict__ partial) {
   constexpr int TT = kLargeTiles;
   static_assert(TT <= kLogitsWaves, "one loading wave per token tile");
+  const int L = blockIdx.x;
+  const int tile = kXcds * (L / (kXcds * kSlices)) + L % kXcds;
+  const int slice = (L / kXcds) % kSlices;
+  const int t0 = tile * kRouteTok * TT;
+  if (t0 >= N) return;                                 // whole workgroup, before any barrier
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int t0 = blockIdx.x * kRouteTok * TT;
   const int nsub = cols / 16;
   const int ksteps = H / 32;
   const int per_slice = (ksteps + kSlices - 1) / kSlices;
-  const int kb = blockIdx.y * per_slice, ke = min(ksteps, kb + per_slice);
+  const int kb = slice * per_slice, ke = min(ksteps, kb + per_slice);
 
   const uint16_t* b_src[SUBW];
   floatx4 acc[TT][SUBW];
@@ -410,7 +438,7 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_bf16_kernel(
     }
     __syncthreads();
   }
-  float* dst = partial + (int64_t)blockIdx.y * N * cols;
+  float* dst = partial + (int64_t)slice * N * cols;
 #pragma unroll
   for (int i = 0; i < SUBW; ++i) {
     const int sub = wave + kLogitsWaves * i;
@@ -463,7 +491,7 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* router_
     const uint16_t *xb = (const uint16_t*)x, *rb = (const uint16_t*)router_w, *gb = (const uint16_t*)shared_gate;
     const int nsub = cols / 16;
     if (N >= kLargeBatch) {
-      const dim3 lgrid((N + kRouteTok * kLargeTiles - 1) / (kRouteTok * kLargeTiles), kSlices);
+      const dim3 lgrid(large_tile_groups(N) * kXcds * kSlices);
       if (cols <= 16 * kLogitsWaves * 3)
         hipLaunchKernelGGL((route_logits_bf16_kernel<3>), lgrid, dim3(kLogitsThreads), 0, s, xb, rb, gb, N, H, E, cols,
                            scratch);
@@ -479,12 +507,13 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* router_
     hipLaunchKernelGGL(route_logits_f32_kernel, lgrid, dim3(kLogitsThreads), 0, s, (const float*)x,
                        (const float*)router_w, (const float*)shared_gate, N, H, E, cols, scratch);
   }
-  const dim3 sgrid((N + kSelectWaves - 1) / kSelectWaves);
+  const bool by_tile = p.dtype == MOE_BF16 && N >= kLargeBatch;
+  const dim3 sgrid(by_tile ? large_tile_groups(N) * kXcds * kSelectPerTile : (N + kSelectWaves - 1) / kSelectWaves);
   const int nw = (int)p.norm_topk_prob;
   auto go = [&](auto per) {
     constexpr int PER = decltype(per)::value;
     hipLaunchKernelGGL(route_select_kernel<PER>, sgrid, dim3(kSelectWaves * kWave), 0, s, scratch, N, E, k, nw,
-                       (int)shared, cols, ids, w, shared_scale);
+                       (int)shared, cols, (int)by_tile, ids, w, shared_scale);
   };
   if (E <= 64) go(std::integral_constant<int, 1>{});
   else if (E <= 128) go(std::integral_constant<int, 2>{});
