@@ -97,6 +97,26 @@ __device__ __forceinline__ void scatter_range(const int (&ev)[kAlignUnroll], int
   }
 }
 
+// Inclusive prefix sum over the 16 lanes of each DPP row (Hillis-Steele,
+// shifts 1, 2, 4, 8; a lane whose source lies before its row adds 0).
+__device__ __forceinline__ int row_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  return v;
+}
+
+// Inclusive prefix sum over the wave: row scans, then each row adds the
+// totals of the rows before it (row_bcast:15 into rows 1 and 3, then
+// row_bcast:31 into rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v = row_inclusive_scan(v);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
 // Wave 0: exclusive scans of cnt[] (rows) and of its tile counts over the
 // experts; writes seg_start, tile_start and (when not null) offsets and
 // num_tiles.
@@ -108,20 +128,15 @@ __device__ __forceinline__ void scan_experts(const int* cnt, int E, int BM, int*
     const int e = e0 + lane;
     const int c = (e < E) ? cnt[e] : 0;
     const int nt = (c + BM - 1) / BM;
-    int ic = c, it = nt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int uc = __shfl_up(ic, o, kWave);
-      const int ut = __shfl_up(it, o, kWave);
-      if (lane >= o) { ic += uc; it += ut; }
-    }
+    const int ic = wave_inclusive_scan(c);
+    const int it = wave_inclusive_scan(nt);
     if (e < E) {
       seg_start[e] = carry_rows + ic - c;
       tile_start[e] = carry_tiles + it - nt;
       if (offsets) offsets[e] = carry_rows + ic - c;
     }
-    carry_rows += __shfl(ic, kWave - 1, kWave);
-    carry_tiles += __shfl(it, kWave - 1, kWave);
+    carry_rows += __builtin_amdgcn_readlane(ic, kWave - 1);
+    carry_tiles += __builtin_amdgcn_readlane(it, kWave - 1);
   }
   if (lane == 0 && offsets) {
     offsets[E] = carry_rows;
@@ -240,6 +255,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_scatter_kernel(
   __shared__ int base[kMaxExperts];
   __shared__ int seg_start[kMaxExperts];
   __shared__ int tile_start[kMaxExperts];
+  __shared__ int part_sum[kAlignThreads];
+  __shared__ int part_before[kAlignThreads];
   __shared__ int total_tiles;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -251,21 +268,53 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_scatter_kernel(
   int ev[kAlignUnroll];
   load_range(ids, beg, end, E, ev);                    // in flight with the chunk counts below
   for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&hist[0][0])[i] = 0;
-  for (int e = tid; e < E; e += kAlignThreads) {
-    int run = 0, mine = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 8) {          // 8 independent loads in flight
+  // Expert totals over all chunks, and this chunk's base in each expert (its
+  // pairs in the chunks before it).  Up to 16 chunks: one thread per
+  // expert, loads in rounds of 8.  More: G groups of E threads each sum a
+  // contiguous run of about 8 chunks, so the loads go out in one round, and
+  // the group sums are added in LDS (measured: the extra barrier costs more
+  // than a second round of loads saves at 16 chunks, and less at 32).
+  auto sum_chunks = [&](int e, int c_lo, int c_hi, int& sum, int& before) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += 8) {         // 8 independent loads in flight
       int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (c0 + u < nchunks) ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+      for (int u = 0; u < 8; ++u) v[u] = (c0 + u < c_hi) ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        if (c0 + u == b) mine = run;                   // pairs of e in the chunks before this one
-        run += v[u];
+        sum += v[u];
+        before += (c0 + u < b) ? v[u] : 0;
       }
     }
-    cnt[e] = run;
-    base[e] = mine;
-    if (lead) counts[e] = run;
+  };
+  if (nchunks <= 16) {
+    for (int e = tid; e < E; e += kAlignThreads) {
+      int run = 0, mine = 0;
+      sum_chunks(e, 0, nchunks, run, mine);
+      cnt[e] = run;
+      base[e] = mine;
+      if (lead) counts[e] = run;
+    }
+  } else {
+    const int G = min(kAlignThreads / E, (nchunks + 7) / 8);   // E <= kMaxExperts <= kAlignThreads / 2
+    const int cpg = (nchunks + G - 1) / G;
+    if (tid < G * E) {
+      const int g = tid / E, e = tid % E;
+      int sum = 0, before = 0;
+      sum_chunks(e, g * cpg, min(nchunks, (g + 1) * cpg), sum, before);
+      part_sum[tid] = sum;
+      part_before[tid] = before;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kAlignThreads) {
+      int run = 0, mine = 0;
+      for (int g = 0; g < G; ++g) {
+        run += part_sum[g * E + e];
+        mine += part_before[g * E + e];
+      }
+      cnt[e] = run;
+      base[e] = mine;
+      if (lead) counts[e] = run;
+    }
   }
   __syncthreads();
   if (tid < kWave) scan_experts(cnt, E, BM, seg_start, tile_start, lead ? offsets : nullptr, num_tiles);
