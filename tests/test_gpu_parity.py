@@ -138,7 +138,9 @@ def test_align_walkthrough_on_gpu():
     (3, 2, 5, 16, "uniform"), (64, 8, 128, 16, "uniform"), (4096, 8, 128, 128, "uniform"),
     (16384, 8, 128, 128, "zipf"), (1000, 4, 7, 32, "one"), (333, 1, 1, 64, "uniform"),
     (1, 8, 8, 16, "uniform"), (5000, 6, 512, 16, "zipf"), (777, 3, 60, 1, "uniform"),
-    (513, 8, 64, 16, "uniform"), (2048, 2, 3, 320, "one"), (9000, 4, 128, 320, "zipf")])
+    (513, 8, 64, 16, "uniform"), (2048, 2, 3, 320, "one"), (9000, 4, 128, 320, "zipf"),
+    # more than 16 chunks of 4096 pairs: the chunk counts are summed by thread groups
+    (12000, 8, 512, 64, "zipf"), (20000, 4, 7, 32, "one"), (70000, 1, 1, 16, "uniform")])
 def test_align_matches_oracle(N, k, E, bm, dist):
     rng = np.random.default_rng(N * 31 + E)
     if dist == "uniform":
