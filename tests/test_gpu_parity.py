@@ -351,7 +351,8 @@ def test_staged_calls_equal_forward():
                                         (4099, 128, 160, 6, 32), (3000, 192, 512, 32, 0)])
 def test_router_tilings_bitwise_equal(N, H, E, k, Is):
     """Batches of 512 tokens and more compute their logits in 64-token
-    tiles (x fragments shared through LDS), smaller ones in 16-token tiles;
+    tiles (x fragments shared through LDS) placed by XCD, smaller ones in
+    one-wave workgroups of 16 tokens and three 16-column sub-tiles;
     a token's ids, weights and shared gate must be bit for bit the same
     whichever batch routed it (also at the layer's own H = 2048 and at
     E = 512)."""
