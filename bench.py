@@ -245,6 +245,40 @@ def prewarm(torch, moe, seconds=1.0):
     torch.cuda.empty_cache()
 
 
+MEASURED_PEAK = {}          # filled by measure_mfma_peak() before the workloads run
+
+
+def measure_mfma_peak(torch, moe, iters=4096, reps=9):
+    """The matrix-unit rate this part sustains: the library's probe (back to
+    back 16x16x32 bf16 matrix instructions on random register operands, 16
+    waves per CU) timed with events on the stream it runs on; median of
+    `reps` launches.  A second reference beside the datasheet peak."""
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(1)
+    ops = torch.randn(1 << 20, generator=g, device=dev).to(torch.bfloat16)
+    sink = torch.empty(moe.MOE_PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        moe.moe_mfma_probe(ops, iters, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    flops = 0.0
+    for e0, e1 in ev:
+        e0.record()
+        flops = moe.moe_mfma_probe(ops, iters, sink)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    tf = flops / (ms * 1e-3) / 1e12
+    MEASURED_PEAK.update({"tflops": round(tf, 1), "frac_of_datasheet": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "launch_ms": round(ms, 4),
+                          "kernel": "16x16x32 bf16 matrix instructions back to back on random register operands, "
+                                    "512 workgroups x 8 waves, 8 independent accumulators per wave"})
+    return dict(MEASURED_PEAK)
+
+
+def of_measured(tflops):
+    return round(tflops / MEASURED_PEAK["tflops"], 4) if MEASURED_PEAK else None
+
+
 def bench_dense(name, steps, warmup, torch, moe):
     """A dense SwiGLU layer (moe_dense_mlp) of hidden 2048, I = 6144."""
     from sparse_moe_ffn_amd.inputs import DENSE_LAYERS, make_dense_inputs
@@ -262,6 +296,7 @@ def bench_dense(name, steps, warmup, torch, moe):
             "steps": steps, "tokens_per_s": round(L["N"] / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
             "step_event_ms": event_summary(per), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_of_measured_peak": of_measured(flops / (ms * 1e-3) / 1e12),
             "weight_hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
@@ -350,7 +385,8 @@ def roofline_for(res):
     common = {"kernel": f"grouped_gemm_bf16 gate_up (SwiGLU epilogue), {tiles}, blocked weights",
               "traffic": measured_traffic(cfg.name), "avg_launch_ms": round(res["stage_ms"][kern], 4),
               "algorithmic_bytes_per_launch": w["bytes"], "algorithmic_flops_per_launch": w["flops"],
-              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+              "mfma_frac_of_measured_peak": of_measured(tfs)}
     if w["bytes"] / (HBM_PEAK_GBS * 1e9) >= w["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12):
         return {**common, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -448,7 +484,9 @@ def leg_summary(r):
            "ms_per_step_row_major": round(r["ms_per_step_row_major"], 4),
            "step_event_ms_row_major": r["step_event_ms_row_major"],
            "tflops": round(r["tflops"], 1), "mfma_frac": round(r["mfma_frac"], 4),
-           "mfma_frac_median": round(r["mfma_frac_median"], 4), "weight_hbm_frac": round(r["weight_hbm_frac"], 4),
+           "mfma_frac_median": round(r["mfma_frac_median"], 4),
+           "mfma_frac_of_measured_peak": of_measured(r["tflops_median"]),
+           "weight_hbm_frac": round(r["weight_hbm_frac"], 4),
            "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
            "stage_median_ms": r["stage_median_ms"], "roofline": roofline_for(r),
            "counts_min_max": r["counts_min_max"], "hit_experts": r["hit_experts"]}
@@ -472,6 +510,8 @@ def main():
         sys.exit(1)
     moe.load_library()
     prewarm(torch, moe)
+    print("[bench] matrix-unit probe", file=sys.stderr, flush=True)
+    measure_mfma_peak(torch, moe)
     print(f"[bench] workload {a.workload}: {a.warmup} warmup + {a.steps} timed steps", file=sys.stderr, flush=True)
     main_res = bench_workload(a.workload, a.steps, a.warmup, torch, moe)
     also = {}
@@ -512,6 +552,7 @@ def main():
         "stage_median_ms": main_res["stage_median_ms"],
         "hit_experts": main_res["hit_experts"],
         "roofline": roofline_for(main_res), "cpu_baseline": cpu, "also": also,
+        "mfma_peak_measured": dict(MEASURED_PEAK),
     }
     print(json.dumps(line), flush=True)
 

@@ -323,6 +323,27 @@ int moe_forward_noalloc(const moe_problem* p, const void* x, const void* router_
                         const void* shared_w_gate_up, const void* shared_w_down,
                         const void* shared_gate, void* out, void* stream);
 
+/* Matrix-unit rate probe (measurement only, not part of the block): one
+ * launch of MOE_PROBE_WORKGROUPS workgroups of 8 waves, each wave running
+ * `iters` rounds of 8 independent 16x16x32 bf16 matrix instructions on
+ * operands it loads once from `operands` into registers; no memory traffic
+ * in the loop.  The products' MFMA fractions are quoted against the
+ * datasheet peak; timing this launch (events on `stream`) gives the rate the
+ * part sustains with realistic, toggling data as a second reference.
+ *   operands:     device, bf16, num_operands elements (>= 512, a multiple of
+ *                 512), ideally random values; read only.
+ *   iters:        1 .. 1048576.
+ *   sink:         device, MOE_PROBE_SINK_FLOATS floats; receives per-lane sums
+ *                 of the accumulators (meaningless values; they keep the loop).
+ *   flops:        host; receives the launch's matrix flops
+ *                 (MOE_PROBE_WORKGROUPS * 8 * 8 * iters * 16384).
+ * Errors: MOE_EINVAL for null pointers or out-of-range sizes (nothing is
+ * enqueued); MOE_EHIP if the launch fails. */
+#define MOE_PROBE_WORKGROUPS 512
+#define MOE_PROBE_SINK_FLOATS (MOE_PROBE_WORKGROUPS * 8 * 64)
+int moe_mfma_probe(const void* operands, int64_t num_operands, int64_t iters, float* sink, double* flops,
+                   void* stream);
+
 /* Message for the last non-zero return on the calling thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -10,4 +10,5 @@ from .binding import (MoEError, MoEProblem, Grouping, load_library, problem, pro
                       moe_route,
                       moe_align, moe_gate_up, moe_down, moe_gate_up_ids, moe_down_ids, moe_shared_expert, moe_combine, moe_forward,
                       moe_dense_mlp, moe_add_rmsnorm, moe_pack_weights, moe_forward_noalloc, MOE_NOALLOC_SCRATCH_BYTES,
+                      moe_mfma_probe, MOE_PROBE_SINK_FLOATS,
                       MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_BLOCKED)

@@ -82,6 +82,7 @@ def load_library() -> ctypes.CDLL:
             "moe_dense_mlp": [PP, _P, _P, _P, _P, _P, _P],
             "moe_add_rmsnorm": [_I64, _I64, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_float, _P, _P],
             "moe_pack_weights": [_I64, _I64, _I64, ctypes.c_int32, _P, _P, _P],
+            "moe_mfma_probe": [_P, _I64, _I64, _P, ctypes.POINTER(ctypes.c_double), _P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -633,3 +634,28 @@ def moe_forward_noalloc(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob, s
                                                   _ptr(w_down), _ptr(shared_w_gate_up), _ptr(shared_w_down),
                                                   _ptr(shared_gate), _ptr(out), _stream(dev)))
     return out
+
+
+MOE_PROBE_WORKGROUPS = 512
+MOE_PROBE_SINK_FLOATS = MOE_PROBE_WORKGROUPS * 8 * 64
+
+
+def moe_mfma_probe(operands, iters, sink=None) -> float:
+    """Enqueue the matrix-unit rate probe on the current stream and return
+    the launch's matrix flops (time it with events on that stream).
+    operands: bf16 GPU tensor, a positive multiple of 512 elements (random
+    values); sink: float32 GPU tensor of MOE_PROBE_SINK_FLOATS (allocated
+    when None)."""
+    ops = _gpu(operands, "operands", torch.bfloat16)
+    if ops.numel() < 512 or ops.numel() % 512:
+        raise ValueError(f"operands must hold a positive multiple of 512 elements, got {ops.numel()}")
+    if sink is None:
+        sink = torch.empty(MOE_PROBE_SINK_FLOATS, dtype=torch.float32, device=ops.device)
+    sink = _gpu(sink, "sink", torch.float32, ops.device)
+    if sink.numel() < MOE_PROBE_SINK_FLOATS:
+        raise ValueError(f"sink must hold {MOE_PROBE_SINK_FLOATS} floats, got {sink.numel()}")
+    flops = ctypes.c_double(0.0)
+    with torch.cuda.device(ops.device):
+        _check(load_library().moe_mfma_probe(_ptr(ops), ops.numel(), int(iters), _ptr(sink), ctypes.byref(flops),
+                                             _stream(ops.device)))
+    return flops.value

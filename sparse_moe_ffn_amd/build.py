@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["route.hip", "align.hip", "grouped_gemm.hip", "combine.hip", "norm.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "align.hip", "grouped_gemm.hip", "combine.hip", "norm.hip", "peak_probe.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 
 

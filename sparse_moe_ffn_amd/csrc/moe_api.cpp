@@ -310,6 +310,17 @@ extern "C" {
 
 const char* moe_last_error(void) { return g_err; }
 
+int moe_mfma_probe(const void* operands, int64_t num_operands, int64_t iters, float* sink, double* flops,
+                   void* stream) {
+  if (!operands || !sink || !flops) return fail(MOE_EINVAL, "null pointer");
+  if (num_operands < 512 || num_operands % 512 != 0)
+    return fail(MOE_EINVAL, "num_operands must be a positive multiple of 512, got %lld", (long long)num_operands);
+  if (iters < 1 || iters > (1 << 20)) return fail(MOE_EINVAL, "iters must be in [1, 1048576], got %lld", (long long)iters);
+  if (!aligned16(operands)) return fail(MOE_EINVAL, "operands must be 16-byte aligned");
+  *flops = moe::mfma_probe_flops(iters);
+  return hip_status(moe::launch_mfma_probe(operands, num_operands, iters, sink, (hipStream_t)stream), "mfma probe");
+}
+
 int moe_align_capacity(int64_t num_pairs, int64_t num_experts, int64_t block_m, int64_t* max_rows,
                        int64_t* max_tiles) {
   if (!max_rows || !max_tiles) return fail(MOE_EINVAL, "output pointer is NULL");

@@ -78,4 +78,10 @@ hipError_t launch_add_rmsnorm(const void* x, const void* residual_in, void* resi
 hipError_t launch_combine(const void* y, const void* shared_y, void* out, int64_t N, int64_t H,
                           int64_t top_k, int32_t dtype, hipStream_t s);
 
+// Matrix-unit rate probe: MOE_PROBE_WORKGROUPS workgroups of back-to-back
+// bf16 matrix instructions on register operands; mfma_probe_flops gives the
+// launch's flop count.
+hipError_t launch_mfma_probe(const void* ops, int64_t num_ops, int64_t iters, float* sink, hipStream_t s);
+double mfma_probe_flops(int64_t iters);
+
 }  // namespace moe

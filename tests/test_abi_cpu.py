@@ -358,3 +358,28 @@ def test_noalloc_scratch_size_matches_header():
     src = open(HEADER).read()
     m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_mfma_probe_rejects_before_any_hip_call():
+    """The matrix-unit probe checks pointers, sizes and alignment before it
+    launches anything."""
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    flops = ctypes.c_double(-1.0)
+    assert lib.moe_mfma_probe(None, 512, 10, fake, ctypes.byref(flops), None) == B.MOE_EINVAL
+    assert lib.moe_mfma_probe(fake, 512, 10, None, ctypes.byref(flops), None) == B.MOE_EINVAL
+    assert lib.moe_mfma_probe(fake, 512, 10, fake, None, None) == B.MOE_EINVAL
+    assert lib.moe_mfma_probe(fake, 0, 10, fake, ctypes.byref(flops), None) == B.MOE_EINVAL
+    assert lib.moe_mfma_probe(fake, 1000, 10, fake, ctypes.byref(flops), None) == B.MOE_EINVAL
+    assert lib.moe_mfma_probe(fake, 512, 0, fake, ctypes.byref(flops), None) == B.MOE_EINVAL
+    assert lib.moe_mfma_probe(fake, 512, (1 << 20) + 1, fake, ctypes.byref(flops), None) == B.MOE_EINVAL
+    assert lib.moe_mfma_probe(ctypes.c_void_p((1 << 20) + 2), 512, 10, fake, ctypes.byref(flops), None) == B.MOE_EINVAL
+    assert b"aligned" in lib.moe_last_error()
+    assert flops.value == -1.0                              # nothing written on an error
+
+
+def test_mfma_probe_constants_match_header():
+    src = open(HEADER).read()
+    assert re.search(r"#define MOE_PROBE_WORKGROUPS (\d+)", src).group(1) == str(B.MOE_PROBE_WORKGROUPS)
+    assert "#define MOE_PROBE_SINK_FLOATS (MOE_PROBE_WORKGROUPS * 8 * 64)" in src
+    assert B.MOE_PROBE_SINK_FLOATS == B.MOE_PROBE_WORKGROUPS * 8 * 64
