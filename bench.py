@@ -43,10 +43,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "skew", "talker"])
-    ap.add_argument("--also", default="prefill,skew,talker,dense_prefill,decode_block",
+    ap.add_argument("--also", default="prefill,skew,talker,dense_prefill,decode_block,ep8_share",
                     help="comma-separated extra workloads ('' for none): prefill, skew, talker, decode, "
                          "dense_prefill, dense_decode (dense SwiGLU layers), decode_block (residual add + "
-                         "RMSNorm + the decode MoE layer, eager and replayed from a HIP graph)")
+                         "RMSNorm + the decode MoE layer, eager and replayed from a HIP graph), ep8_share "
+                         "(one GPU's expert-parallel share of an 8 x 4096-token prefill batch)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle budget: whole passes over the main workload on all cores for about this "
                          "long, then a single-thread sample of a third of it (0: skip)")
@@ -300,6 +301,57 @@ def bench_dense(name, steps, warmup, torch, moe):
             "weight_hbm_frac": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def bench_ep_share(steps, warmup, torch, moe, gpus=8):
+    """One GPU's share of the prefill layer under expert parallelism over
+    `gpus` GPUs (expert e on GPU e mod gpus), run on this one GPU: the global
+    batch is gpus x 4096 tokens, every GPU's router is run here (untimed) and
+    torch indexing stands in for the dispatch all-to-all, so this GPU holds
+    the x rows of the pairs routed to its E/gpus experts.  The timed step is
+    what that GPU computes: moe_align over the received pairs (local expert
+    ids, one row per pair), then the grouped gate/up and down products.  The
+    y rows would then go back to their tokens' GPUs for the combine."""
+    from sparse_moe_ffn_amd.inputs import CONFIGS, make_inputs
+
+    base = CONFIGS["prefill"]
+    cfg = base.with_(name="ep_global", N=base.N * gpus)
+    t = make_inputs(cfg, "cuda:0")
+    ids, w, _ = moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    flat_ids, flat_w = ids.reshape(-1), w.reshape(-1)
+    sel = torch.nonzero(flat_ids % gpus == 0).squeeze(1)          # pairs sent to GPU 0, pair order
+    P, E_loc = sel.numel(), cfg.E // gpus
+    x_recv = t["x"][torch.div(sel, cfg.top_k, rounding_mode="floor")].contiguous()
+    ids_local = torch.div(flat_ids[sel], gpus, rounding_mode="floor").to(torch.int32).view(-1, 1).contiguous()
+    w_recv = flat_w[sel].contiguous()
+    wgu = moe.moe_pack_weights(t["w_gate_up"][0::gpus].contiguous())
+    wd = moe.moe_pack_weights(t["w_down"][0::gpus].contiguous())
+    del t, ids, w, flat_ids, flat_w
+    torch.cuda.empty_cache()
+    bm = moe.moe_get_workspace_layout(moe.problem(P, cfg.H, E_loc, 1, cfg.I))["block_m"]
+    blk = moe.MOE_LAYOUT_BLOCKED
+    gr = moe.moe_align(ids_local, E_loc, bm)
+    act = moe.moe_gate_up(x_recv, wgu, gr, 1, weight_layout=blk)
+    y = moe.moe_down(act, wd, w_recv, gr, P, 1, weight_layout=blk)
+
+    def step():
+        g = moe.moe_align(ids_local, E_loc, bm)
+        moe.moe_gate_up(x_recv, wgu, g, 1, act=act, weight_layout=blk)
+        moe.moe_down(act, wd, w_recv, g, P, 1, y=y, weight_layout=blk)
+
+    ms, per = timed_steps(step, steps, warmup, torch)
+    counts = gr.counts.cpu()
+    ev = event_summary(per)
+    flops = 6.0 * P * cfg.H * cfg.I
+    tf = flops / (ev["median"] * 1e-3) / 1e12
+    wbytes = E_loc * 3 * cfg.H * cfg.I * 2
+    return {"workload": f"ep{gpus}_share: GPU 0 of {gpus} (experts e mod {gpus} == 0) in the {cfg.N}-token prefill "
+                        f"batch: {P} received pairs over {E_loc} local experts, H={cfg.H} I={cfg.I} bf16, "
+                        "step = align + gate/up + down (route, all-to-all and combine not on this GPU's path)",
+            "steps": steps, "pairs": P, "block_m": bm, "counts_min_max": [int(counts.min()), int(counts.max())],
+            "ms_per_step": round(ms, 4), "step_event_ms": ev, "tflops_median": round(tf, 1),
+            "mfma_frac_median": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "mfma_frac_of_measured_peak": of_measured(tf),
+            "weight_bytes": wbytes}
+
+
 def bench_decode_block(steps, warmup, torch, moe):
     """Residual add + RMSNorm, then the decode MoE layer, issued eagerly and
     replayed from one captured HIP graph."""
@@ -523,6 +575,10 @@ def main():
             continue
         if w == "decode_block":
             also[w] = bench_decode_block(a.steps, a.warmup, torch, moe)
+            torch.cuda.empty_cache()
+            continue
+        if w == "ep8_share":
+            also[w] = bench_ep_share(a.steps, a.warmup, torch, moe)
             torch.cuda.empty_cache()
             continue
         r = bench_workload(w, a.steps, a.warmup, torch, moe)
