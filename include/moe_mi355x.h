@@ -144,7 +144,8 @@ int moe_align_capacity(int64_t num_pairs, int64_t num_experts, int64_t block_m,
  *   topk_w     [N, k]  float32 out: the probabilities of those experts,
  *                      divided by their sum when norm_topk_prob is set
  *   scratch            float32 device array of moe_route_scratch_size bytes
- *                      (partial logits; overwritten, need not be cleared)
+ *                      (partial logits; overwritten, need not be cleared),
+ *                      16-byte aligned in bf16
  * Logits are accumulated in float32 (8 fixed slices of H, summed in slice
  * order, so a token's routing does not depend on the batch); softmax runs
  * over all E in float32. */

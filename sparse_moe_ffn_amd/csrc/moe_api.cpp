@@ -376,7 +376,7 @@ int moe_route(const moe_problem* p, const void* x, const void* router_w, const v
   if (p->num_tokens == 0) return ok();
   if (!x || !router_w || !topk_ids || !topk_w || !scratch) return fail(MOE_EINVAL, "NULL tensor");
   if (shared_gate && !shared_scale) return fail(MOE_EINVAL, "shared_gate given without shared_scale");
-  if (int rc = check_ptrs_bf16(p, {x, router_w, shared_gate})) return rc;
+  if (int rc = check_ptrs_bf16(p, {x, router_w, shared_gate, scratch})) return rc;   // partials: 16-byte stores
   if (int rc = hip_status(moe::launch_route(*p, x, router_w, shared_gate, topk_ids, topk_w,
                                             shared_scale, scratch, (hipStream_t)stream), "route"))
     return rc;

@@ -287,8 +287,11 @@ __global__ __launch_bounds__(kSelectWaves * kWave) void route_select_kernel(
 // row_c = router_w[c] for c < E, the shared gate for c == E, zero beyond.
 // Every logit is one chain of matrix instructions over the slice's 32-wide
 // k-steps in increasing order, from a zero accumulator, whichever kernel
-// and tile computes it, so both tilings give the same bits.  A lane holds 4
-// rows of one column of each 16x16 sub-tile.
+// and tile computes it, so both tilings give the same bits.  The router
+// rows are the matrix instruction's first operand and the tokens its second
+// (the transposed product: same products and sums, measured bit for bit
+// equal), so a lane holds 4 adjacent columns of one token of each 16x16
+// sub-tile and writes them with one 16-byte store.
 
 // Column c's router row, offset to this lane's 8-element piece, or null.
 __device__ __forceinline__ const uint16_t* router_row(const uint16_t* router_w, const uint16_t* shared_gate, int c,
@@ -340,20 +343,15 @@ __global__ __launch_bounds__(kWave) void route_logits_small_bf16_kernel(
     for (int u = 0; u < kUnroll; ++u)
       if (s0 + u < ke) {
 #pragma unroll
-        for (int i = 0; i < kSmallSub; ++i) acc[i] = mfma16x16x32(a[u], b[u][i], acc[i]);
+        for (int i = 0; i < kSmallSub; ++i) acc[i] = mfma16x16x32(b[u][i], a[u], acc[i]);
       }
   }
   float* dst = partial + (int64_t)blockIdx.y * N * cols;
 #pragma unroll
   for (int i = 0; i < kSmallSub; ++i) {
-    if (sub0 + i < nsub) {
-      const int c = (sub0 + i) * 16 + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = t0 + (lane >> 4) * 4 + r;
-        if (n < N) dst[(int64_t)n * cols + c] = acc[i][r];
-      }
-    }
+    const int n = t0 + (lane & 15);
+    if (sub0 + i < nsub && n < N)
+      *reinterpret_cast<floatx4*>(dst + (int64_t)n * cols + (sub0 + i) * 16 + (lane >> 4) * 4) = acc[i];
   }
 }
 
@@ -432,7 +430,7 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_bf16_kernel(
           const uint4 af = a_lds[t][u][lane];
 #pragma unroll
           for (int i = 0; i < SUBW; ++i)
-            if (wave + kLogitsWaves * i < nsub) acc[t][i] = mfma16x16x32(af, b[u][i], acc[t][i]);
+            if (wave + kLogitsWaves * i < nsub) acc[t][i] = mfma16x16x32(b[u][i], af, acc[t][i]);
         }
       }
     }
@@ -443,14 +441,11 @@ __global__ __launch_bounds__(kLogitsThreads) void route_logits_bf16_kernel(
   for (int i = 0; i < SUBW; ++i) {
     const int sub = wave + kLogitsWaves * i;
     if (sub < nsub) {
-      const int c = sub * 16 + (lane & 15);
+      const int c = sub * 16 + (lane >> 4) * 4;         // 4 adjacent columns of one token
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = t0 + t * 16 + (lane >> 4) * 4 + r;
-          if (n < N) dst[(int64_t)n * cols + c] = acc[t][i][r];
-        }
+        const int n = t0 + t * 16 + (lane & 15);
+        if (n < N) *reinterpret_cast<floatx4*>(dst + (int64_t)n * cols + c) = acc[t][i];
       }
     }
   }

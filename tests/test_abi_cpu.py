@@ -383,3 +383,14 @@ def test_mfma_probe_constants_match_header():
     assert re.search(r"#define MOE_PROBE_WORKGROUPS (\d+)", src).group(1) == str(B.MOE_PROBE_WORKGROUPS)
     assert "#define MOE_PROBE_SINK_FLOATS (MOE_PROBE_WORKGROUPS * 8 * 64)" in src
     assert B.MOE_PROBE_SINK_FLOATS == B.MOE_PROBE_WORKGROUPS * 8 * 64
+
+
+def test_route_rejects_misaligned_scratch_before_any_hip_call():
+    """The router writes its partial logits with 16-byte stores, so a bf16
+    call with a scratch pointer that is not 16-byte aligned is refused before
+    anything is launched."""
+    lib = moe.load_library()
+    p = moe.problem(64, 2048, 128, 8, 768)
+    fake = ctypes.c_void_p(1 << 20)
+    rc = lib.moe_route(ctypes.byref(p), fake, fake, None, fake, fake, None, ctypes.c_void_p((1 << 20) + 4), None)
+    assert rc == B.MOE_EUNSUPPORTED and b"aligned" in lib.moe_last_error()
