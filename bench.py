@@ -16,10 +16,13 @@ by one.  ``cpu_baseline`` times the CPU oracle on a bounded token sample.
 ``also`` holds the same figures for the other workloads given with --also
 (by default the 4096-token prefill layer, the 16384-token skewed layer with
 its expert-load report, the 8192-token talker layer with a shared expert, a
-dense SwiGLU layer and the graph-replayed decode block), each timed over the
-same number of steps as the main workload.  Every step time is given as the
-wall-clock mean over the timed steps and as the median / min / mean of
-per-step HIP events.
+dense SwiGLU layer, the graph-replayed decode block and one GPU's
+expert-parallel share of an 8 x 4096-token prefill batch), each timed over
+the same number of steps as the main workload.  Every step time is given as
+the wall-clock mean over the timed steps, run back to back, and as the
+median / min / mean of per-step HIP events from a second loop of the same
+steps.  ``mfma_peak_measured`` is the matrix-unit rate the library's probe
+sustains in the same run, a second reference beside the datasheet peak.
 """
 from __future__ import annotations
 
@@ -80,21 +83,26 @@ def kernel_work(cfg, counts):
 
 
 def timed_steps(fn, steps, warmup, torch):
-    """Run `warmup` untimed steps, then exactly `steps` timed ones between two
-    device synchronisations.  Returns the wall-clock mean per step (ms) and
-    the per-step HIP-event durations (ms), recorded on torch's current stream
-    (the stream every call is enqueued on)."""
+    """Run `warmup` untimed steps, then exactly `steps` timed ones back to
+    back between two device synchronisations: the wall-clock mean per step
+    (ms).  Then the same number of steps again with a HIP event recorded
+    after each one on torch's current stream (the stream every call is
+    enqueued on): the per-step durations (ms).  The events sit in a loop of
+    their own because each record adds a few microseconds to a step."""
     for _ in range(warmup):
         fn()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record()
     for i in range(steps):
         fn()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps * 1e3
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     return wall, per
 
