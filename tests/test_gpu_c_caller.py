@@ -26,7 +26,7 @@ def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     moe.load_library()
-    if not os.path.exists(EXE):                      # normally built by __graft_entry__.build()
+    if not os.path.exists(EXE):                      # normally built beside the library (tests/c/build.py)
         spec = importlib.util.spec_from_file_location("c_caller_build", os.path.join(HERE, "c", "build.py"))
         mod = importlib.util.module_from_spec(spec)
         spec.loader.exec_module(mod)
