@@ -302,7 +302,7 @@ int moe_forward(const moe_problem* p, const void* x, const void* router_w,
 
 /* Bytes of the fixed scratch array behind moe_forward_noalloc (64 MiB per
  * GPU).  At the Qwen3-30B-A3B layer shape (H=2048, E=128, top-8, I=768) that
- * holds the workspace of batches up to about a thousand tokens. */
+ * holds the workspace of batches up to about 800 tokens. */
 #define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* The whole block without any allocation, for callers that cannot call

@@ -83,13 +83,23 @@ int check_problem(const moe_problem* p, unsigned uses = kUsesAll) {
   return MOE_OK;
 }
 
+// Row-tile height of the grouped products, from the pairs per expert the
+// host can see (avg = N*k / E): the shortest height that holds nearly every
+// expert's pairs in one tile, since a second tile re-reads the expert's
+// weights, while taller tiles only add padding rows.  The boundaries are
+// measured (H=2048, E=128, top-8, I=768, blocked weights; route + align +
+// products + combine), e.g. 160 tokens (avg 10): 16-row tiles 214.4 us,
+// 32-row 204.4; 256 (avg 16): 238.6 / 210.5 (16 / 32); 384 (avg 24): 235.3 /
+// 220.4 (32 / 64); 720 (avg 45): 268.3 / 242.3 (64 / 128); 1024 (avg 64):
+// 291.3 / 252.5 (64 / 128); 1900 (avg 119): 305.4 / 319.5 (128 / 320);
+// 2048 (avg 128): 338.2 / 322.9 (128 / 320).
 int64_t choose_block_m(const moe_problem* p) {
   if (p->dtype == MOE_F32) return 16;
   const double avg = (double)(p->num_tokens * p->top_k) / (double)p->num_experts;
-  if (avg < 24) return 16;
-  if (avg < 48) return 32;
-  if (avg < 96) return 64;
-  if (avg < 192) return 128;
+  if (avg < 9) return 16;
+  if (avg < 20) return 32;
+  if (avg < 42) return 64;
+  if (avg < 124) return 128;
   return 320;                       // one tile holds a typical prefill expert
 }
 

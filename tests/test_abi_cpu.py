@@ -53,8 +53,12 @@ def test_workspace_layout_is_ordered_and_aligned():
 
 
 def test_block_m_follows_rows_per_expert():
+    """The shortest tile that holds nearly every expert's pairs: 16 / 32 / 64 /
+    128 / 320 rows below 9 / 20 / 42 / 124 pairs per expert and above."""
     bm = lambda N: moe.moe_get_workspace_layout(moe.problem(N, 2048, 128, 8, 768))["block_m"]
-    assert (bm(64), bm(1024), bm(4096), bm(16384)) == (16, 64, 320, 320)
+    Ns = (64, 128, 160, 256, 384, 640, 720, 1024, 1900, 2048, 4096, 16384)
+    assert tuple(bm(N) for N in Ns) == (16, 16, 32, 32, 64, 64, 128, 128, 128, 320, 320, 320)
+    assert moe.moe_get_workspace_layout(moe.problem(1000, 256, 16, 8, 128, dtype=torch.float32))["block_m"] == 16
 
 
 @pytest.mark.parametrize("pairs,E,bm", [(6, 5, 2), (512, 128, 16), (32768, 128, 128), (3, 10, 64), (0, 4, 16)])

@@ -37,7 +37,7 @@ def fits(cfg, t):
 PAIRS = [
     (CONFIGS["decode"], random_case(20, 2048, 128, 8, 768, seed=3)),
     (random_case(700, 256, 32, 4, 128, I_shared=64, seed=4), random_case(1, 256, 32, 4, 128, I_shared=64, seed=5)),
-    (random_case(900, 2048, 128, 8, 768, seed=6), CONFIGS["decode"]),
+    (random_case(800, 2048, 128, 8, 768, seed=6), CONFIGS["decode"]),
     (CONFIGS["tiny"], random_case(3, 64, 6, 2, 128, dtype="f32", seed=7)),
 ]
 
