@@ -103,16 +103,24 @@ int64_t choose_block_m(const moe_problem* p) {
   return 320;                       // one tile holds a typical prefill expert
 }
 
-// Row-tile height of the dense products (shared expert, dense layers): tall
-// tiles (fewer bytes per flop) once there are enough rows to fill the GPU
-// with them.  Measured on the talker's shared expert (8192 rows, I_s = 2048):
-// 320-row tiles 199 us, 128-row tiles 218 us, 64-row tiles 308 us.
-int64_t dense_block_m(const moe_problem* p) {
+// Row-tile height of the dense products (shared expert, dense layers) for
+// `inter` gate and up columns: the tallest tile (fewest bytes per flop)
+// whose gate/up launch still keeps at least half of the GPU's 256 CUs busy,
+// ceil(N / h) row tiles times the column blocks (128 gate and 128 up columns
+// per workgroup from 64 rows up, 64 and 64 below) >= 128 workgroups.
+// Measured on the dense SwiGLU layer (H=2048, I=6144, blocked weights):
+// 64 tokens 32-row tiles 55.1 us against 68.1 with 16 rows; 128 tokens
+// 32 rows 68.2 against 93.4 with 64; 1024 tokens 320 rows 126.9 against
+// 138.8 with 128; 3072 tokens 320 rows 207.5 against 274.7 with 128.  The
+// talker's shared expert (8192 rows, I_s = 2048) keeps 320-row tiles (416
+// workgroups; 128-row tiles took 218 against 199 us there).
+int64_t dense_block_m(const moe_problem* p, int64_t inter) {
   if (p->dtype == MOE_F32) return 16;
   const int64_t N = p->num_tokens;
-  if (N >= 4096) return 320;
-  if (N >= 512) return 128;
-  if (N >= 128) return 64;
+  for (int64_t h : {320, 128, 64, 32}) {
+    const int64_t cols = (h >= 64) ? 128 : 64;        // gate (and as many up) columns per workgroup
+    if (((N + h - 1) / h) * ((inter + cols - 1) / cols) >= 128) return h;
+  }
   return 16;
 }
 
@@ -238,7 +246,7 @@ void dense_problems(const moe_problem* p, int64_t inter, const void* x, const vo
                     const float* scale, void* act, void* c, moe::GemmProblem* gu, moe::GemmProblem* dn,
                     bool fill_down = true) {
   const int64_t N = p->num_tokens;
-  const int64_t bm = dense_block_m(p);
+  const int64_t bm = dense_block_m(p, inter);
   moe::GemmProblem g = gemm_common(p);
   g.dense_rows = (int32_t)N;
   g.block_m = (int32_t)bm;
@@ -571,7 +579,7 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
   const bool shared = shared_w_gate_up != nullptr;
   // The shared expert joins the routed products' launches when both run the
   // same bf16 tile height.
-  const bool merge_shared = shared && !L.ids_products && p->dtype == MOE_BF16 && dense_block_m(p) == L.block_m;
+  const bool merge_shared = shared && !L.ids_products && p->dtype == MOE_BF16 && dense_block_m(p, p->shared_inter) == L.block_m;
   auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
   int32_t* ids = (int32_t*)at(L.topk_ids);
   float* w = (float*)at(L.topk_w);

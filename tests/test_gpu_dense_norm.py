@@ -40,11 +40,15 @@ def check(out, ref, dtype, what):
 
 # ------------------------------------------------------------ dense SwiGLU
 
-# The trailing comments give the row-tile height the library picks.
+# The trailing comments give the gate/up row-tile height the library picks
+# (the tallest that still fills half the CUs) and the down height where it
+# differs.  Every case ends in a ragged row tile.
 DENSE_SMALL = [(1, 64, 64, "bf16"), (37, 128, 192, "bf16"),            # 16
-               (200, 256, 128, "bf16"), (333, 192, 448, "bf16"),       # 64
-               (1300, 1024, 2048, "bf16"),                             # 128
-               (4100, 128, 64, "bf16"), (4200, 256, 320, "bf16"),      # 320, ragged last tile
+               (200, 256, 128, "bf16"), (333, 192, 448, "bf16"),       # 16
+               (200, 256, 1472, "bf16"), (4100, 128, 64, "bf16"),      # 32
+               (600, 128, 2048, "bf16"), (4200, 256, 320, "bf16"),     # 64
+               (1300, 1024, 2048, "bf16"),                             # 128 (down 64)
+               (700, 128, 5440, "bf16"),                               # 320 (down 64), ragged column block
                (5, 24, 40, "f32"), (70, 33, 17, "f32")]
 
 

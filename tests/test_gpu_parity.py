@@ -313,15 +313,20 @@ def test_batch_invariance_decode_layer():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,sizes", [("prefill", [1, 64, 600, 1024, 2048]), ("talker", [1, 24, 600, 4096])])
+@pytest.mark.parametrize("name,sizes", [("prefill", [1, 64, 200, 600, 1024, 2048]),
+                                        ("talker", [1, 24, 100, 200, 600, 1000, 2000, 4096])])
 def test_batch_invariance_across_tile_heights(name, sizes):
     """A token's output is the same bit for bit in any batch.  The first n
-    tokens of the layer run, by batch size, 16-row tiles (1 token), the ids
-    products (24 or 64), 32-, 64- and 128-row tiles (600, 1024, 2048) and
-    320-row tiles (4096 and the whole batch); with the shared expert its
-    dense products change tile height too.  Routing sums fixed H slices and
-    every product sums each output element in one K order whatever its tile,
-    so the rows must agree exactly."""
+    tokens of the layer run, by batch size, 16-row grouped tiles (1 token),
+    the ids products (24 to 100), 32-row tiles (200), 64-row tiles (600),
+    128-row tiles (1000, 1024) and 320-row tiles (2000 and up, the whole
+    batch included).  The talker's shared expert takes its own dense tile
+    height: 16 rows up to 24 tokens, then 32, 32, 64, 128, 128 and 320 rows,
+    in one launch with the routed tiles where the heights agree (1, 200,
+    600, 1000, 4096 and the whole batch) and in launches of its own where
+    they do not.  Routing sums fixed H slices and every product sums each
+    output element in one K order whatever its tile, so the rows must agree
+    exactly."""
     cfg, t = full_inputs(name)
     full = run_forward(t, cfg)
     for n in sizes:
