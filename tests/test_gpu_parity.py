@@ -353,7 +353,8 @@ def test_staged_calls_equal_forward():
 
 @pytest.mark.parametrize("N,H,E,k,Is", [(700, 256, 128, 8, 64), (523, 128, 64, 4, 0), (1031, 192, 160, 6, 32),
                                         (2048, 2048, 128, 8, 0), (2100, 256, 128, 8, 64),
-                                        (4099, 128, 160, 6, 32), (3000, 192, 512, 32, 0)])
+                                        (4099, 128, 160, 6, 32), (3000, 192, 512, 32, 0),
+                                        (8200, 128, 128, 8, 64), (16400, 64, 128, 8, 64)])
 def test_router_tilings_bitwise_equal(N, H, E, k, Is):
     """Batches of 512 tokens and more compute their logits in 64-token
     tiles (x fragments shared through LDS) placed by XCD, smaller ones in
@@ -368,6 +369,8 @@ def test_router_tilings_bitwise_equal(N, H, E, k, Is):
     windows = [(0, 64), (N - 37, N), (511, 512)]
     if N >= 2048:
         windows += [(N - 1100, N - 3), (1500, 1600)]               # 64-token tiles; 16-token tiles
+    if N >= 8192:
+        windows += [(N - 2100, N - 1), (5, 8200)]                  # other tile and XCD alignments
     for lo, hi in windows:
         ids_s, w_s, sc_s = moe.moe_route(t["x"][lo:hi].contiguous(), t["router_w"], k, True, gate)
         torch.cuda.synchronize()
