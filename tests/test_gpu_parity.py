@@ -303,6 +303,39 @@ def test_larger_layer_shape(N):
 
 
 @pytest.mark.slow
+def test_offsets_past_32_bits():
+    """A batch of 2^18 + 37 tokens of the 30B-A3B layer shape (H=2048,
+    E=128, top-8, I=768): the (token, slot) rows of y then hold more than
+    2^32 elements, and tokens from 2^18 on have all their down outputs and
+    combine inputs past element 2^32, so any 32-bit offset in the down
+    epilogue, the combine or the grouping would show in their rows.  Their
+    ids, weights and outputs, and those of a few tokens before, are
+    compared with the oracle's per-token definition."""
+    N = (1 << 18) + 37
+    cfg = random_case(N, 2048, 128, 8, 768, dtype="bf16", seed=41)
+    assert N * cfg.top_k * cfg.H > 1 << 32
+    t = make_inputs(cfg, DEV)
+    out = run_forward(t, cfg)
+    ids_gpu, w_gpu, _ = moe.moe_route(t["x"], t["router_w"], cfg.top_k, cfg.norm_topk_prob)
+    torch.cuda.synchronize()
+    sample = [0, 1, N // 2, (1 << 18) - 1] + list(range(1 << 18, N))
+    idx = torch.tensor(sample, device=DEV)
+    xs = host(t["x"][idx])
+    rw = host(t["router_w"])
+    routing = O.route(xs, rw, cfg.top_k, cfg.norm_topk_prob)
+    ids_ref, w_ref, _, margin = routing
+    keep = margin >= MARGIN
+    ids_s = ids_gpu[idx].cpu().numpy()
+    w_s = w_gpu[idx].cpu().numpy()
+    assert (ids_s[keep] == ids_ref[keep]).all(), "routed ids differ"
+    np.testing.assert_allclose(w_s[keep], w_ref[keep], rtol=2e-5, atol=2e-6)
+    ref, _ = O.moe_forward(xs, rw, host(t["w_gate_up"]), host(t["w_down"]), cfg.top_k, cfg.norm_topk_prob,
+                           routing=routing)
+    err, tol = check_output(host(out[idx])[keep], ref[keep], cfg.dtype, cfg.name)
+    print(f"{cfg.name}: {int(keep.sum())} of {len(sample)} sampled tokens compared, err {err:.3e} tol {tol:.3e}")
+
+
+@pytest.mark.slow
 def test_batch_invariance_decode_layer():
     cfg, t = full_inputs("decode")
     full = run_forward(t, cfg)
