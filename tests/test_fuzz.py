@@ -12,7 +12,7 @@ counts that are not multiples of any tile height.
 """
 import numpy as np
 import pytest
-from hypothesis import HealthCheck, given, settings
+from hypothesis import HealthCheck, example, given, settings
 from hypothesis import strategies as st
 
 from oracle import moe_oracle as O
@@ -140,3 +140,49 @@ def test_forward_fuzz(s):
     tol = O.tolerance(ref[keep], cfg.dtype)
     err = float(np.abs(got[keep] - ref[keep]).max()) if keep.any() else 0.0
     assert err <= tol, f"{cfg.name}: max|gpu-ref| = {err:.3e} > {tol:.3e}"
+
+
+@st.composite
+def dense_shapes(draw):
+    H = draw(st.sampled_from([64, 128, 256]))
+    I = 64 * draw(st.integers(1, 48))
+    N = draw(st.sampled_from([1, 17, 100, 333, 700, 1500, 2100, 4100]))
+    while N * H * I > 4e8 and N > 1:
+        N //= 2
+    return dict(N=N, H=H, I=I, seed=draw(st.integers(0, 10_000)), blocked=draw(st.booleans()))
+
+
+@pytest.mark.gpu
+@settings(FUZZ, max_examples=30)
+@given(dense_shapes())
+@example(dict(N=4100, H=64, I=1280, seed=1, blocked=True))       # 320-row tiles
+@example(dict(N=2100, H=64, I=1024, seed=2, blocked=False))      # 128
+@example(dict(N=700, H=128, I=1472, seed=3, blocked=True))       # 64, ragged column block
+@example(dict(N=333, H=64, I=1024, seed=4, blocked=False))       # 32
+@example(dict(N=17, H=256, I=64, seed=5, blocked=True))          # 16
+def test_dense_mlp_fuzz(s):
+    """The dense SwiGLU layer on random shapes in both weight layouts.  The
+    row-tile height follows the batch and the intermediate width (16 to 320
+    rows, the tallest that still fills the GPU); the explicit examples take
+    each height once, with ragged last row tiles, and the draws add more."""
+    import torch
+
+    import sparse_moe_ffn_amd as moe
+    from sparse_moe_ffn_amd.inputs import make_dense_inputs
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"dense fuzz case N={s['N']} H={s['H']} I={s['I']} seed={s['seed']} blocked={s['blocked']}", flush=True)
+    t = make_dense_inputs(s["N"], s["H"], s["I"], seed=s["seed"], device="cuda:0")
+    wgu, wd = t["w_gate_up"], t["w_down"]
+    lay = moe.MOE_LAYOUT_ROW_MAJOR
+    if s["blocked"]:
+        wgu, wd, lay = moe.moe_pack_weights(wgu), moe.moe_pack_weights(wd), moe.MOE_LAYOUT_BLOCKED
+    out = moe.moe_dense_mlp(t["x"], wgu, wd, weight_layout=lay)
+    torch.cuda.synchronize()
+    ref = O.dense_mlp(_np(t["x"].cpu()), _np(t["w_gate_up"].cpu()), _np(t["w_down"].cpu()))
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    tol = O.tolerance(ref, "bf16")
+    err = float(np.abs(got - ref).max())
+    assert err <= tol, f"dense N{s['N']} H{s['H']} I{s['I']}: max|gpu-ref| = {err:.3e} > {tol:.3e}"
