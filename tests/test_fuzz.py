@@ -8,7 +8,8 @@ counts sum to N*k, padded tiles of one expert each).
 
 GPU: the whole HIP path against the oracle on random shapes, including
 N = 1, k = 1, k = E, experts that get no pairs, a shared expert, and row
-counts that are not multiples of any tile height.
+counts that are not multiples of any tile height; and the dense SwiGLU
+layer on random shapes in both weight layouts.
 """
 import numpy as np
 import pytest
