@@ -544,12 +544,18 @@ _workspaces = {}
 
 
 def workspace_for(p: MoEProblem, device) -> torch.Tensor:
-    """A cached uint8 workspace large enough for `p` on `device`."""
+    """A cached uint8 workspace large enough for `p`, one per (device,
+    current stream).  Calls on one stream run in order and can share it;
+    calls on different streams may run at the same time, so each stream has
+    its own.  The workspace is allocated on that stream, so when it grows,
+    torch's allocator reuses the old block only for later work on the same
+    stream."""
     need = moe_workspace_size(p)
-    key = torch.device(device)
+    dev = torch.device(device)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=key)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -581,7 +587,8 @@ def moe_forward(x, router_w, w_gate_up, w_down, top_k, norm_topk_prob=True, shar
                 shared_w_down=None, shared_gate=None, out=None, workspace=None, weight_layout=MOE_LAYOUT_ROW_MAJOR):
     """The whole block: out [N, H] in x.dtype.  With weight_layout
     MOE_LAYOUT_BLOCKED the expert (and shared-expert) weights are the
-    outputs of moe_pack_weights."""
+    outputs of moe_pack_weights.  Without `workspace`, the cached workspace
+    of the current stream is used (workspace_for)."""
     _check_forward_shapes(x, router_w, w_gate_up, w_down, shared_w_gate_up, shared_w_down, shared_gate, out)
     p = problem_from(x, w_gate_up, router_w, top_k, norm_topk_prob, shared_w_gate_up, weight_layout)
     if workspace is not None:
