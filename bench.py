@@ -82,6 +82,51 @@ def kernel_work(cfg, counts):
     }
 
 
+def stage_work(cfg, counts, block_m, ids_path):
+    """Algorithmic bytes and flops of every stage of one step (the staged
+    calls of bench_workload), for the per-stage roofline.
+
+    route: x and the router rows (plus the shared gate) read once, ids and
+    weights (plus the shared scale) written; flops 2*H per logit.
+    align: the N*k ids read, the stable order and the padded pair list
+    written (int32).  gate_up, down: kernel_work.  shared: the shared
+    expert's weights and x read once, its act written and read, its output
+    row written; flops 2*H*2I_s + 2*I_s*H per token.  combine: the k rows of
+    y per token (plus the shared row) read, the output row written.
+    """
+    es = 2 if cfg.dtype == "bf16" else 4
+    N, H, E, k, Is = cfg.N, cfg.H, cfg.E, cfg.top_k, cfg.I_shared
+    P = N * k
+    cols = E + (1 if Is else 0)
+    w = dict(kernel_work(cfg, counts))
+    w["route"] = {"bytes": N * H * es + cols * H * es + P * 8 + (N * 4 if Is else 0), "flops": 2.0 * N * H * cols}
+    if not ids_path:
+        padded = int(sum(-(-int(c) // block_m) * block_m for c in counts))
+        w["align"] = {"bytes": P * 4 + P * 4 + padded * 4, "flops": 0.0}
+    if Is:
+        w["shared"] = {"bytes": 3 * Is * H * es + N * H * es + 2 * N * Is * es + N * H * es,
+                       "flops": 2.0 * N * H * 2 * Is + 2.0 * N * Is * H}
+    w["combine"] = {"bytes": P * H * es + N * H * es + (N * H * es if Is else 0), "flops": 0.0}
+    return w
+
+
+def stage_roofline(res):
+    """Each stage's median time against the roof that bounds it (the longer
+    of bytes at the HBM peak and flops at the bf16 MFMA peak)."""
+    out = {}
+    for name, ms in res["stage_median_ms"].items():
+        w = res["stage_work"].get(name)
+        if w is None or ms <= 0:
+            continue
+        t = ms * 1e-3
+        hbm_t = w["bytes"] / (HBM_PEAK_GBS * 1e9)
+        mfma_t = w["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        bound = "hbm" if hbm_t >= mfma_t else "mfma"
+        out[name] = {"ms": round(ms, 5), "bytes": int(w["bytes"]), "flops": w["flops"], "bound": bound,
+                     "frac": round(max(hbm_t, mfma_t) / t, 4)}
+    return out
+
+
 def timed_steps(fn, steps, warmup, torch):
     """Run `warmup` untimed steps, then exactly `steps` timed ones back to
     back between two device synchronisations: the wall-clock mean per step
@@ -218,13 +263,15 @@ def bench_workload(name, steps, warmup, torch, moe):
                        for i, name_ in enumerate(stages)}
     counts = moe.moe_align(ids, cfg.E, bm, align_scratch).counts.cpu().numpy()   # untimed: pairs per expert
     work = kernel_work(cfg, counts)
+    swork = stage_work(cfg, counts, bm, ids_path)
     ms = wall
     res = {
         "cfg": cfg, "inputs": t, "ms_per_step": ms, "tokens_per_s": cfg.N / (ms * 1e-3),
         "step_event_ms": event_summary(per), "ms_per_step_row_major": ms_row_major,
         "step_event_ms_row_major": event_summary(per_rm),
         "tflops": cfg.flops() / (ms * 1e-3) / 1e12, "stage_ms": stage_ms, "stage_median_ms": stage_median_ms,
-        "work": work, "hit_experts": expert_hits(counts), "counts_min_max": [int(counts.min()), int(counts.max())],
+        "work": work, "stage_work": swork, "hit_experts": expert_hits(counts),
+        "counts_min_max": [int(counts.min()), int(counts.max())],
         "block_m": bm, "ids_path": ids_path, "counts": counts, "steps": steps,
     }
     med = res["step_event_ms"]["median"]
@@ -548,7 +595,7 @@ def leg_summary(r):
            "mfma_frac_of_measured_peak": of_measured(r["tflops_median"]),
            "weight_hbm_frac": round(r["weight_hbm_frac"], 4),
            "stage_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()},
-           "stage_median_ms": r["stage_median_ms"], "roofline": roofline_for(r),
+           "stage_median_ms": r["stage_median_ms"], "stage_roofline": stage_roofline(r), "roofline": roofline_for(r),
            "counts_min_max": r["counts_min_max"], "hit_experts": r["hit_experts"]}
     if cfg.skew:
         out["load"] = load_report(r["counts"], cfg)
@@ -614,6 +661,7 @@ def main():
         "weight_hbm_frac": round(main_res["weight_hbm_frac"], 4),
         "stage_ms": {k: round(v, 4) for k, v in main_res["stage_ms"].items()},
         "stage_median_ms": main_res["stage_median_ms"],
+        "stage_roofline": stage_roofline(main_res),
         "hit_experts": main_res["hit_experts"],
         "roofline": roofline_for(main_res), "cpu_baseline": cpu, "also": also,
         "mfma_peak_measured": dict(MEASURED_PEAK),
