@@ -1,4 +1,5 @@
-"""Degenerate routing on the HIP path: every expert equally likely.
+"""Degenerate inputs on the HIP path: every expert equally likely, and a
+token with non-finite inputs.
 
 With a zero router weight every logit is exactly 0, so every expert has
 probability exactly 1/E and the top-k is decided by the tie rule alone:
@@ -10,6 +11,9 @@ run experts whose weights several row tiles share.  Ids, weights and counts
 must be exact; outputs within |gpu - ref| <= 2e-2 * max|ref| + 1e-3 in bf16,
 1e-4 * max|ref| in fp32 against the oracle (which breaks ties the same way:
 a stable sort of the probabilities).
+
+A token whose input row holds NaN or Inf must leave every other token's
+output bit for bit unchanged (its own row is non-finite).
 """
 import numpy as np
 import pytest
@@ -75,3 +79,31 @@ def test_all_equal_probabilities_take_the_lowest_ids(cfg):
     assert np.isfinite(got).all()
     err = float(np.abs(got - ref).max())
     assert err <= tol, f"max|gpu-ref| = {err:.4e} > tol {tol:.4e}"
+
+
+# ------------------------------------------------------------- non-finite input
+
+@pytest.mark.parametrize("cfg,bad", [
+    (random_case(64, 2048, 128, 8, 768, seed=41), 17),                           # the ids products
+    (random_case(700, 256, 16, 4, 128, I_shared=64, seed=42), 333),              # grouped tiles + shared expert
+    (random_case(700, 256, 16, 4, 128, seed=43, norm_topk_prob=False), 0),       # no renormalisation
+], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+@pytest.mark.parametrize("value", [float("nan"), float("inf")])
+def test_non_finite_token_is_contained(cfg, bad, value):
+    """A token whose input row holds NaN or Inf gets a non-finite output row
+    and changes no other token's output: every row of an expert tile is
+    computed on its own, in the expert's fixed K order, so the other rows
+    must be bit for bit those of the batch without the bad token's values
+    (that token routed differently only moves rows between tiles)."""
+    t = make_inputs(cfg, DEV)
+    args = (t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob, t["shared_w_gate_up"],
+            t["shared_w_down"], t["shared_gate"])
+    clean = moe.moe_forward(t["x"], *args)
+    x = t["x"].clone()
+    x[bad, :: 3] = value
+    dirty = moe.moe_forward(x, *args)
+    torch.cuda.synchronize()
+    keep = torch.ones(cfg.N, dtype=torch.bool, device=DEV)
+    keep[bad] = False
+    assert torch.equal(dirty[keep], clean[keep]), "a non-finite token changed other tokens' outputs"
+    assert not torch.isfinite(dirty[bad]).any(), "the non-finite token's output row is finite"
