@@ -208,11 +208,31 @@ def test_forward_small(cfg):
 
 
 def test_empty_batch():
-    cfg = random_case(4, 64, 4, 2, 64, dtype="bf16")
+    """N = 0 is a no-op for every entry point: each returns empty outputs
+    of the right shape without an error."""
+    cfg = random_case(4, 64, 4, 2, 64, I_shared=64, dtype="bf16")
     t = make_inputs(cfg, DEV)
     x0 = t["x"][:0]
     out = moe.moe_forward(x0, t["router_w"], t["w_gate_up"], t["w_down"], 2, True)
     assert out.shape == (0, 64)
+    out = moe.moe_forward(x0, t["router_w"], t["w_gate_up"], t["w_down"], 2, True, t["shared_w_gate_up"],
+                          t["shared_w_down"], t["shared_gate"])
+    assert out.shape == (0, 64)
+    out = moe.moe_forward_noalloc(x0, t["router_w"], t["w_gate_up"], t["w_down"], 2, True)
+    assert out.shape == (0, 64)
+    ids, w, sc = moe.moe_route(x0, t["router_w"], 2, True, t["shared_gate"])
+    assert ids.shape == (0, 2) and w.shape == (0, 2) and sc.shape == (0,)
+    gr = moe.moe_align(ids, cfg.E, 16)
+    assert int(gr.counts.sum()) == 0
+    act = moe.moe_gate_up(x0, t["w_gate_up"], gr, 2)
+    y = moe.moe_down(act, t["w_down"], w, gr, 0, 2)
+    assert moe.moe_combine(y, 0, 2).shape == (0, 64)
+    sa, sy = moe.moe_shared_expert(x0, t["shared_w_gate_up"], t["shared_w_down"], sc)
+    assert sy.shape == (0, 64)
+    assert moe.moe_dense_mlp(x0, t["shared_w_gate_up"], t["shared_w_down"]).shape == (0, 64)
+    normed, res = moe.moe_add_rmsnorm(x0, torch.empty_like(x0), t["shared_gate"])
+    assert normed.shape == (0, 64) and res.shape == (0, 64)
+    torch.cuda.synchronize()
 
 
 # --------------------------------------------------------------- full-size workloads
