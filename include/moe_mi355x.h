@@ -96,6 +96,11 @@ typedef struct moe_workspace_layout {
   int64_t max_tiles;       /* capacity of tile_expert / tile_rows */
   int64_t ids_products;    /* 1: moe_forward runs moe_gate_up_ids / moe_down_ids
                               (no grouping; act rows are pair indices) */
+  int64_t shared_block_m;  /* rows per tile of the shared expert's gate/up
+                              product (0 without a shared expert) */
+  int64_t shared_merged;   /* 1: moe_forward runs the shared expert's products
+                              in the routed products' launches (grouped bf16
+                              products of the same tile height) */
   size_t route_scratch, topk_ids, topk_w, shared_scale;
   size_t counts, offsets, order, sorted_pairs, tile_expert, tile_rows, num_tiles, align_scratch;
   size_t act, y, shared_act, shared_y;

@@ -42,7 +42,8 @@ class MoEProblem(ctypes.Structure):
 
 class MoEWorkspaceLayout(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int64), ("max_rows", ctypes.c_int64), ("max_tiles", ctypes.c_int64),
-                ("ids_products", ctypes.c_int64)] + [
+                ("ids_products", ctypes.c_int64), ("shared_block_m", ctypes.c_int64),
+                ("shared_merged", ctypes.c_int64)] + [
         (n, ctypes.c_size_t) for n in ("route_scratch", "topk_ids", "topk_w", "shared_scale", "counts", "offsets",
                                        "order",
                                        "sorted_pairs", "tile_expert", "tile_rows", "num_tiles", "align_scratch",

@@ -124,25 +124,30 @@ int64_t dense_block_m(const moe_problem* p, int64_t inter) {
   return 16;
 }
 
-// Row-tile height of a dense down product: the gate/up height, lowered (to
-// 128, then 64 rows) while its tiles (times the 256-column blocks of H)
-// would leave more than half of the GPU's 256 CUs idle.  The down product's
-// K (the intermediate size) is long for dense layers, so such a launch keeps
-// most CUs idle throughout: the dense layer's down (4096 x 6144 -> 2048) ran
-// 104 workgroups of 320 rows; with 128-row tiles, 256 (dense layer 0.333 ->
-// 0.286 ms).  At 208 workgroups (the talker's shared expert, 8192 rows) the
-// 320-row tiles stay faster (196 against 207 us for both products).  Every
-// tile height sums each element in one K order, so the result does not
-// change.
+// Row-tile height of a dense down product: the tallest height up to the
+// gate/up one whose launch still has 160 workgroups, ceil(N / h) row tiles
+// times the column blocks of H (256 columns from 64 rows up, 128 below),
+// else the shortest of them down to 32 rows.  The down product's K (the
+// intermediate size) is long for dense layers, so a launch with few
+// workgroups keeps most CUs idle throughout.  Measured on the dense SwiGLU
+// layer (H=2048, I=6144, blocked weights), whole layer: 256 tokens 32-row
+// down tiles 72.8 us against 99.3 with 64; 512 tokens 32 rows 76.6 against
+// 101.9 with 64; 1024 tokens 32 rows 109.4 against 126.8 with 64; 1280
+// tokens 64 rows 126.0 against 140.5 with 32; 2048 tokens 64 rows 189.0
+// against 201.0 with 128; 2560 tokens 128 rows 204.7 against 252.0 with
+// 64; 4096 tokens 128 rows 278.3 against 321.4 with 64.  16-row tiles were
+// never faster than 32-row ones there, so they are left to 16-row gate/up
+// tiles.  Every tile height sums each element in one K order, so the result
+// does not change.
 int64_t dense_down_block_m(const moe_problem* p, int64_t bm) {
   if (p->dtype == MOE_F32) return bm;
-  const int64_t N = p->num_tokens, col_blocks = (p->hidden + 255) / 256;
-  static const int64_t heights[] = {320, 128, 64};    // not below 64 rows: thin tiles re-read the weight
+  const int64_t N = p->num_tokens, H = p->hidden;
   int64_t chosen = bm;
-  for (int64_t h : heights) {
+  for (int64_t h : {320, 128, 64, 32}) {
     if (h > bm) continue;
     chosen = h;
-    if (((N + h - 1) / h) * col_blocks >= 128) break;
+    const int64_t cols = (h >= 64) ? 256 : 128;       // output columns per workgroup
+    if (((N + h - 1) / h) * ((H + cols - 1) / cols) >= 160) break;
   }
   return chosen;
 }
@@ -184,6 +189,9 @@ void layout_of(const moe_problem* p, moe_workspace_layout* L) {
   L->block_m = choose_block_m(p);
   capacity(P, E, L->block_m, &L->max_rows, &L->max_tiles);
   L->ids_products = scan_mode(p, *L) ? 1 : 0;
+  L->shared_block_m = p->shared_inter > 0 ? dense_block_m(p, p->shared_inter) : 0;
+  L->shared_merged = (p->shared_inter > 0 && !L->ids_products && p->dtype == MOE_BF16 &&
+                      L->shared_block_m == L->block_m) ? 1 : 0;
   size_t off = 0;
   auto region = [&](size_t bytes) {
     off = (off + 255) & ~(size_t)255;
@@ -579,7 +587,7 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
   const bool shared = shared_w_gate_up != nullptr;
   // The shared expert joins the routed products' launches when both run the
   // same bf16 tile height.
-  const bool merge_shared = shared && !L.ids_products && p->dtype == MOE_BF16 && dense_block_m(p, p->shared_inter) == L.block_m;
+  const bool merge_shared = shared && L.shared_merged;
   auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
   int32_t* ids = (int32_t*)at(L.topk_ids);
   float* w = (float*)at(L.topk_w);

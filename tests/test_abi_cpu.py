@@ -398,3 +398,19 @@ def test_route_rejects_misaligned_scratch_before_any_hip_call():
     fake = ctypes.c_void_p(1 << 20)
     rc = lib.moe_route(ctypes.byref(p), fake, fake, None, fake, fake, None, ctypes.c_void_p((1 << 20) + 4), None)
     assert rc == B.MOE_EUNSUPPORTED and b"aligned" in lib.moe_last_error()
+
+
+def test_shared_expert_tile_height_and_merge():
+    """The layout reports the shared expert's tile height and whether
+    moe_forward runs its products in the routed launches (host arithmetic)."""
+    L = lambda *a, **kw: moe.moe_get_workspace_layout(moe.problem(*a, **kw))
+    talker = L(8192, 2048, 128, 8, 768, 2048)          # routed 320, shared 320
+    assert (talker["block_m"], talker["shared_block_m"], talker["shared_merged"]) == (320, 320, 1)
+    small = L(64, 2048, 128, 8, 768, 2048)             # the ids products: never merged
+    assert small["ids_products"] == 1 and small["shared_merged"] == 0 and small["shared_block_m"] == 16
+    plain = L(4096, 2048, 128, 8, 768)                 # no shared expert
+    assert (plain["shared_block_m"], plain["shared_merged"]) == (0, 0)
+    apart = L(700, 192, 300, 8, 64, 192)               # routed 32, shared 16
+    assert (apart["block_m"], apart["shared_block_m"], apart["shared_merged"]) == (32, 16, 0)
+    f32 = L(4100, 128, 8, 2, 64, 1280, dtype=torch.float32)
+    assert f32["shared_merged"] == 0

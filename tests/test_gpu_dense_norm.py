@@ -42,13 +42,15 @@ def check(out, ref, dtype, what):
 
 # The trailing comments give the gate/up row-tile height the library picks
 # (the tallest that still fills half the CUs) and the down height where it
-# differs.  Every case ends in a ragged row tile.
+# differs (the tallest that gives 160 workgroups, else 32 rows).  Every case
+# ends in a ragged row tile.
 DENSE_SMALL = [(1, 64, 64, "bf16"), (37, 128, 192, "bf16"),            # 16
                (200, 256, 128, "bf16"), (333, 192, 448, "bf16"),       # 16
                (200, 256, 1472, "bf16"), (4100, 128, 64, "bf16"),      # 32
-               (600, 128, 2048, "bf16"), (4200, 256, 320, "bf16"),     # 64
-               (1300, 1024, 2048, "bf16"),                             # 128 (down 64)
-               (700, 128, 5440, "bf16"),                               # 320 (down 64), ragged column block
+               (600, 128, 2048, "bf16"), (4200, 256, 320, "bf16"),     # 64 (down 32)
+               (2500, 1024, 512, "bf16"),                              # 64
+               (1300, 1024, 2048, "bf16"),                             # 128 (down 32)
+               (700, 128, 5440, "bf16"),                               # 320 (down 32), ragged column block
                (5, 24, 40, "f32"), (70, 33, 17, "f32")]
 
 
@@ -59,6 +61,23 @@ def test_dense_mlp_small(N, H, I, dtype):
     torch.cuda.synchronize()
     ref = O.dense_mlp(host(t["x"]), host(t["w_gate_up"]), host(t["w_down"]))
     check(host(out), ref, dtype, f"dense N{N} H{H} I{I} {dtype}")
+
+
+@pytest.mark.parametrize("N,H,I", [(2900, 4096, 1664),    # gate/up and down 320-row tiles
+                                   (4096, 2048, 6144),    # 320 / 128
+                                   (2048, 2048, 6144),    # 320 / 64
+                                   (512, 2048, 6144),     # 128 / 32
+                                   (64, 2048, 6144)])     # 32 / 32
+def test_dense_tile_heights_bitwise(N, H, I):
+    """Rows of a dense layer computed alone (16-row tiles for both products)
+    equal the same rows inside the batch, whose tiles are taller, bit for
+    bit: every tile height sums each element in one K order."""
+    t = make_dense_inputs(N, H, I, seed=N + H, device=DEV)
+    full = moe.moe_dense_mlp(t["x"], t["w_gate_up"], t["w_down"])
+    for lo, hi in ((0, 3), (N - 2, N)):
+        part = moe.moe_dense_mlp(t["x"][lo:hi].contiguous(), t["w_gate_up"], t["w_down"])
+        torch.cuda.synchronize()
+        assert torch.equal(part, full[lo:hi]), f"rows [{lo}, {hi}) differ from the batch of {N}"
 
 
 @pytest.mark.slow

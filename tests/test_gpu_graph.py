@@ -23,18 +23,19 @@ def _need_gpu():
 
 
 CASES = [
-    # N, H, E, k, I, I_shared: N*k > 4096 pairs (several align chunks), 128-row tiles
-    (1000, 256, 64, 8, 128, 0),
+    # N, H, E, k, I, I_shared, shared expert in the routed launches:
+    # N*k > 4096 pairs (several align chunks), 128-row tiles
+    (1000, 256, 72, 8, 128, 0, 0),
     # 320-row tiles, shared expert in the routed launches
-    (4200, 256, 16, 2, 128, 256),
-    # one align workgroup, 32-row tiles, shared expert in 64-row launches of its own
-    (300, 192, 32, 4, 64, 128),
+    (4200, 256, 16, 2, 128, 1280, 1),
+    # one align workgroup, 64-row tiles, shared expert in 16-row launches of its own
+    (300, 192, 32, 4, 64, 128, 0),
 ]
 
 
-@pytest.mark.parametrize("N,H,E,k,I,Is", CASES)
+@pytest.mark.parametrize("N,H,E,k,I,Is,merged", CASES)
 @pytest.mark.parametrize("noalloc", [False, True])
-def test_forward_graph_replays_equal_eager(N, H, E, k, I, Is, noalloc):
+def test_forward_graph_replays_equal_eager(N, H, E, k, I, Is, merged, noalloc):
     cfg = random_case(N, H, E, k, I, I_shared=Is, dtype="bf16", seed=5)
     t = make_inputs(cfg, DEV)
     xs = [make_inputs(cfg.with_(seed=s), DEV)["x"] for s in (11, 12, 13)]
@@ -42,6 +43,7 @@ def test_forward_graph_replays_equal_eager(N, H, E, k, I, Is, noalloc):
     w = {n: (moe.moe_pack_weights(t[n]) if t[n] is not None else None)
          for n in ("w_gate_up", "w_down", "shared_w_gate_up", "shared_w_down")}
     p = moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], k, cfg.norm_topk_prob, t["shared_w_gate_up"], blk)
+    assert moe.moe_get_workspace_layout(p)["shared_merged"] == merged
     if noalloc and moe.moe_workspace_size(p) > moe.MOE_NOALLOC_SCRATCH_BYTES:
         pytest.skip("beyond the allocation-free entry point's scratch")
     ws = torch.empty(moe.moe_workspace_size(p), dtype=torch.uint8, device=DEV)

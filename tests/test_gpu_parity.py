@@ -457,13 +457,19 @@ def test_forward_multichunk_grouping_equals_staged(N, H, E, k, I, Is):
     assert torch.equal(out, ref)
 
 
-@pytest.mark.parametrize("N,H,E,k,I,Is", [(4100, 128, 8, 2, 64, 192), (200, 128, 16, 4, 192, 128),
-                                          (1300, 256, 32, 8, 128, 64), (8192, 256, 128, 8, 128, 256),
-                                          (700, 192, 300, 8, 64, 192)])
-def test_forward_with_shared_equals_staged(N, H, E, k, I, Is):
+@pytest.mark.parametrize("N,H,E,k,I,Is,height,merged", [
+    (4100, 128, 8, 2, 64, 1280, 320, 1),      # routed and shared tiles both 320 rows: one launch per product
+    (1000, 128, 80, 8, 64, 2048, 128, 1),
+    (600, 128, 128, 8, 64, 1664, 64, 1),
+    (200, 128, 128, 8, 64, 1216, 32, 1),
+    (140, 128, 128, 8, 64, 128, 16, 1),       # grouped 16-row tiles (N*k > 1024)
+    (700, 192, 300, 8, 64, 192, 16, 0),       # routed 32, shared 16: launches of its own
+])
+def test_forward_with_shared_equals_staged(N, H, E, k, I, Is, height, merged):
     """moe_forward runs the shared expert's products in the routed products'
-    launches when both take the same tile height (all but the last case
-    here); the output must equal the staged public calls bit for bit."""
+    launches when both take the same tile height (every case here but the
+    last, one per height); the output must equal the staged public calls,
+    whose shared expert runs its own tile heights, bit for bit."""
     cfg = random_case(N, H, E, k, I, I_shared=Is, dtype="bf16", seed=23)
     t = make_inputs(cfg, DEV)
     for layout in (moe.MOE_LAYOUT_ROW_MAJOR, moe.MOE_LAYOUT_BLOCKED):
@@ -475,6 +481,7 @@ def test_forward_with_shared_equals_staged(N, H, E, k, I, Is):
                               tw["shared_w_gate_up"], tw["shared_w_down"], tw["shared_gate"], weight_layout=layout)
         lay = moe.moe_get_workspace_layout(moe.problem_from(t["x"], t["w_gate_up"], t["router_w"], k,
                                                             cfg.norm_topk_prob, t["shared_w_gate_up"]))
+        assert (lay["shared_block_m"], lay["shared_merged"]) == (height, merged)
         ids, w, sc = moe.moe_route(t["x"], t["router_w"], k, cfg.norm_topk_prob, t["shared_gate"])
         if lay["ids_products"]:
             act = moe.moe_gate_up_ids(t["x"], tw["w_gate_up"], ids, weight_layout=layout)
