@@ -701,12 +701,25 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
     else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, kRot, true>(g, g1, s);
     else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, kRot, true>(g, g1, s);
   }
+  // Grouped launches (the routed experts, alone or with the shared expert's
+  // tiles) take 8 waves at 32 and 64 rows; dense launches keep the shapes
+  // below.  Whole forward, H=2048, E=128, top-8, I=768, blocked weights:
+  // 160 / 256 tokens (32-row tiles) 199.9 / 205.5 us against 202.3 / 208.5
+  // with 32x128 tiles of 4 waves; 400 / 640 tokens (64-row tiles) 215.4 /
+  // 230.8 us against 218.9 / 235.7 with 4 waves.  A dense layer (one weight,
+  // few row tiles) lost up to 30% with them: 32x256 tiles halve its
+  // workgroups.
+  const bool grouped = g.sorted_pairs != nullptr || (g1.max_tiles && g1.sorted_pairs != nullptr);
   switch (g.block_m) {
     case 16:   // small batches; down one weight slot shorter (75 -> 74 us)
       if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
       else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE>(g, g1, s);
-    case 32: return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, g1, s);
-    case 64: return launch_bf16<64, 256, 64, 1, 4, 2, 3, MODE>(g, g1, s);
+    case 32:
+      if (grouped) return launch_bf16<32, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);
+      return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, g1, s);
+    case 64:
+      if (grouped) return launch_bf16<64, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);
+      return launch_bf16<64, 256, 64, 1, 4, 2, 3, MODE>(g, g1, s);
     case 128: return launch_bf16<128, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);
     case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE>(g, g1, s);
     default: return hipErrorInvalidValue;
