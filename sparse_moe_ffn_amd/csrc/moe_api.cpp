@@ -86,18 +86,22 @@ int check_problem(const moe_problem* p, unsigned uses = kUsesAll) {
 // Row-tile height of the grouped products, from the pairs per expert the
 // host can see (avg = N*k / E): the shortest height that holds nearly every
 // expert's pairs in one tile, since a second tile re-reads the expert's
-// weights, while taller tiles only add padding rows.  The boundaries are
-// measured (H=2048, E=128, top-8, I=768, blocked weights; route + align +
-// products + combine), e.g. 160 tokens (avg 10): 16-row tiles 214.4 us,
-// 32-row 204.4; 256 (avg 16): 238.6 / 210.5 (16 / 32); 384 (avg 24): 235.3 /
-// 220.4 (32 / 64); 720 (avg 45): 268.3 / 242.3 (64 / 128); 1024 (avg 64):
-// 291.3 / 252.5 (64 / 128); 1900 (avg 119): 305.4 / 319.5 (128 / 320);
-// 2048 (avg 128): 338.2 / 322.9 (128 / 320).
+// weights, while taller tiles only add padding rows; 16-row tiles only
+// while experts average under 2 pairs, where their doubled column blocks
+// (twice the workgroups) still pay.  The boundaries are measured (H=2048,
+// E=128, top-8, I=768, blocked weights; route + align + products +
+// combine): 136 tokens (avg 8.5) 16-row tiles 211.9 us, 32-row 199.5; at
+// E=512, 80 tokens (avg 1.25) 527.2 / 529.0 and 144 tokens (avg 2.25)
+// 645.6 / 643.2 (16 / 32); 256 tokens (avg 16) 205.8 / 209.1 and 264 (avg
+// 16.5) 230.4 / 209.6 (32 / 64: past 16 pairs a few experts need a second
+// 32-row tile, and the launch a fourth round of workgroups); 640 (avg 40)
+// 232.1 / 239.3 and 704 (avg 44) 260.8 / 242.3 (64 / 128); 1900 (avg 119)
+// 299.0 / 319.5 and 2048 (avg 128) 335.9 / 321.8 (128 / 320).
 int64_t choose_block_m(const moe_problem* p) {
   if (p->dtype == MOE_F32) return 16;
   const double avg = (double)(p->num_tokens * p->top_k) / (double)p->num_experts;
-  if (avg < 9) return 16;
-  if (avg < 20) return 32;
+  if (avg < 2) return 16;
+  if (avg <= 16) return 32;
   if (avg < 42) return 64;
   if (avg < 124) return 128;
   return 320;                       // one tile holds a typical prefill expert
@@ -177,18 +181,20 @@ bool ids_supported(const moe_problem* p) {
 // are hit: measured with H=2048, E=128, top-8, blocked weights (moe_forward
 // against the grouped stages), 1 token 64 against 58 us, 16 tokens 152
 // against 138 us, 24 tokens 167 against 175 us, 64 tokens 193 against
-// 204 us, 128 tokens 214 against 218 us.  Taken from N*k >= 1.5 E.
-bool scan_mode(const moe_problem* p, const moe_workspace_layout& L) {
-  return L.block_m == 16 && ids_supported(p) && 2 * p->num_tokens * p->top_k >= 3 * p->num_experts;
+// 204 us, 128 tokens 214 against 218 us.  Taken from N*k >= 1.5 E, while
+// experts average under 9 pairs.
+bool scan_mode(const moe_problem* p) {
+  const int64_t P = p->num_tokens * p->top_k;
+  return ids_supported(p) && 2 * P >= 3 * p->num_experts && P < 9 * p->num_experts;
 }
 
 void layout_of(const moe_problem* p, moe_workspace_layout* L) {
   memset(L, 0, sizeof(*L));
   const int64_t N = p->num_tokens, P = N * p->top_k, E = p->num_experts;
   const size_t es = elt_size(p->dtype);
-  L->block_m = choose_block_m(p);
+  L->ids_products = scan_mode(p) ? 1 : 0;
+  L->block_m = L->ids_products ? 16 : choose_block_m(p);   // the ids products run 16-row passes
   capacity(P, E, L->block_m, &L->max_rows, &L->max_tiles);
-  L->ids_products = scan_mode(p, *L) ? 1 : 0;
   L->shared_block_m = p->shared_inter > 0 ? dense_block_m(p, p->shared_inter) : 0;
   L->shared_merged = (p->shared_inter > 0 && !L->ids_products && p->dtype == MOE_BF16 &&
                       L->shared_block_m == L->block_m) ? 1 : 0;

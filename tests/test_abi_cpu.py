@@ -53,11 +53,13 @@ def test_workspace_layout_is_ordered_and_aligned():
 
 
 def test_block_m_follows_rows_per_expert():
-    """The shortest tile that holds nearly every expert's pairs: 16 / 32 / 64 /
-    128 / 320 rows below 9 / 20 / 42 / 124 pairs per expert and above."""
-    bm = lambda N: moe.moe_get_workspace_layout(moe.problem(N, 2048, 128, 8, 768))["block_m"]
-    Ns = (64, 128, 160, 256, 384, 640, 720, 1024, 1900, 2048, 4096, 16384)
-    assert tuple(bm(N) for N in Ns) == (16, 16, 32, 32, 64, 64, 128, 128, 128, 320, 320, 320)
+    """Grouped tiles: 16 rows below 2 pairs per expert, 32 up to 16, 64
+    below 42, 128 below 124, else 320.  The ids products (most experts hit,
+    under 9 pairs each, at most 1024 pairs) report their 16-row passes."""
+    bm = lambda N, E=128: moe.moe_get_workspace_layout(moe.problem(N, 2048, E, 8, 768))["block_m"]
+    Ns = (16, 64, 128, 136, 160, 256, 264, 384, 640, 720, 1024, 1900, 2048, 4096, 16384)
+    assert tuple(bm(N) for N in Ns) == (16, 16, 16, 32, 32, 32, 64, 64, 64, 128, 128, 128, 320, 320, 320)
+    assert (bm(90, 512), bm(129, 512)) == (16, 32)       # grouped at avg 1.4 and 2.02
     assert moe.moe_get_workspace_layout(moe.problem(1000, 256, 16, 8, 128, dtype=torch.float32))["block_m"] == 16
 
 
@@ -184,9 +186,9 @@ def test_ids_products_reject_before_any_hip_call():
 
 
 def test_forward_schedule_choice():
-    """moe_forward takes the ids products for bf16 batches the grouped path
-    would run in 16-row tiles, with 4 <= N*k <= 1024, N*k % 4 == 0 and
-    N*k >= 1.5 E (most experts hit); otherwise the grouping."""
+    """moe_forward takes the ids products for bf16 batches with
+    4 <= N*k <= 1024, N*k % 4 == 0, N*k >= 1.5 E (most experts hit) and
+    N*k < 9 E (under 9 pairs per expert); otherwise the grouping."""
     import torch
     L = lambda *a, **kw: moe.moe_get_workspace_layout(moe.problem(*a, **kw))["ids_products"]
     assert [L(N, 2048, 128, 8, 768) for N in (1, 16, 23, 24, 64, 128, 129, 4096)] == [0, 0, 0, 1, 1, 1, 0, 0]
@@ -194,6 +196,8 @@ def test_forward_schedule_choice():
     assert L(5, 128, 4, 3, 64) == 0                     # 15 pairs: not a multiple of 4
     assert L(4, 128, 6, 2, 64) == 0                     # 8 pairs: 2 * 8 < 3 * 6
     assert L(6, 128, 6, 2, 64) == 1                     # 12 pairs: 2 * 12 >= 3 * 6
+    assert L(100, 2048, 512, 8, 768) == 1               # 800 pairs over 512 experts
+    assert L(120, 256, 64, 8, 64) == 0                  # 960 pairs: 15 per expert, grouped 32-row tiles
 
 
 # ------------------------------------------------- binding shape checks (no GPU)
@@ -410,7 +414,7 @@ def test_shared_expert_tile_height_and_merge():
     assert small["ids_products"] == 1 and small["shared_merged"] == 0 and small["shared_block_m"] == 16
     plain = L(4096, 2048, 128, 8, 768)                 # no shared expert
     assert (plain["shared_block_m"], plain["shared_merged"]) == (0, 0)
-    apart = L(700, 192, 300, 8, 64, 192)               # routed 32, shared 16
-    assert (apart["block_m"], apart["shared_block_m"], apart["shared_merged"]) == (32, 16, 0)
+    apart = L(700, 192, 300, 8, 64, 192)               # routed 64, shared 16
+    assert (apart["block_m"], apart["shared_block_m"], apart["shared_merged"]) == (64, 16, 0)
     f32 = L(4100, 128, 8, 2, 64, 1280, dtype=torch.float32)
     assert f32["shared_merged"] == 0
