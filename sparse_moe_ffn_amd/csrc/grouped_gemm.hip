@@ -708,14 +708,19 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
   // with 32x128 tiles of 4 waves; 400 / 640 tokens (64-row tiles) 215.4 /
   // 230.8 us against 218.9 / 235.7 with 4 waves.  A dense layer (one weight,
   // few row tiles) lost up to 30% with them: 32x256 tiles halve its
-  // workgroups.
+  // workgroups.  A dense down launch at 16 and 32 rows takes 64-column
+  // tiles (twice the workgroups over its long K): dense layer (H=2048,
+  // I=6144) at 16 / 32 / 64 tokens 52.0 / 53.2 / 54.3 us against 58.5 /
+  // 56.4 / 55.3 with 128 columns.
   const bool grouped = g.sorted_pairs != nullptr || (g1.max_tiles && g1.sorted_pairs != nullptr);
   switch (g.block_m) {
-    case 16:   // small batches; down one weight slot shorter (75 -> 74 us)
+    case 16:   // small batches; grouped down one weight slot shorter (75 -> 74 us)
       if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
+      else if (!grouped) return launch_bf16<16, 64, 64, 1, 4, 2, 4, MODE>(g, g1, s);
       else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE>(g, g1, s);
     case 32:
       if (grouped) return launch_bf16<32, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);
+      if constexpr (MODE == kDown) return launch_bf16<32, 64, 64, 1, 4, 2, 4, MODE>(g, g1, s);
       return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, g1, s);
     case 64:
       if (grouped) return launch_bf16<64, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);

@@ -130,7 +130,7 @@ int64_t dense_block_m(const moe_problem* p, int64_t inter) {
 
 // Row-tile height of a dense down product: the tallest height up to the
 // gate/up one whose launch still has 160 workgroups, ceil(N / h) row tiles
-// times the column blocks of H (256 columns from 64 rows up, 128 below),
+// times the column blocks of H (256 columns from 64 rows up, 64 below),
 // else the shortest of them down to 32 rows.  The down product's K (the
 // intermediate size) is long for dense layers, so a launch with few
 // workgroups keeps most CUs idle throughout.  Measured on the dense SwiGLU
@@ -150,7 +150,7 @@ int64_t dense_down_block_m(const moe_problem* p, int64_t bm) {
   for (int64_t h : {320, 128, 64, 32}) {
     if (h > bm) continue;
     chosen = h;
-    const int64_t cols = (h >= 64) ? 256 : 128;       // output columns per workgroup
+    const int64_t cols = (h >= 64) ? 256 : 64;        // output columns per workgroup
     if (((N + h - 1) / h) * ((H + cols - 1) / cols) >= 160) break;
   }
   return chosen;
