@@ -290,11 +290,11 @@ int moe_combine(const moe_problem* p, const void* y, const void* shared_y,
                 void* out, void* stream);
 
 /* The whole block: moe_route, moe_align, moe_gate_up, moe_down,
- * [moe_shared_expert], moe_combine on one stream, in that order (for batches
- * the grouped products would run in 16-row tiles, that moe_gate_up_ids
- * takes and that reach most experts, N*k >= 1.5 E: moe_route,
- * moe_gate_up_ids, moe_down_ids, [moe_shared_expert], moe_combine, with the
- * same output bit for bit), with every
+ * [moe_shared_expert], moe_combine on one stream, in that order (for bf16
+ * batches that moe_gate_up_ids takes, that reach most experts, N*k >= 1.5 E,
+ * with under 9 pairs per expert, N*k < 9 E: moe_route, moe_gate_up_ids,
+ * moe_down_ids, [moe_shared_expert], moe_combine, with the same output bit
+ * for bit; moe_workspace_layout.ids_products says which), with every
  * intermediate in `workspace` (moe_workspace_size bytes, 256-byte aligned,
  * laid out as moe_get_workspace_layout says).  shared_w_gate_up == NULL means
  * no shared expert (then shared_w_down and shared_gate are ignored and

@@ -69,8 +69,9 @@ def test_ids_products_equal_grouped_rows(cfg, ties, layout):
 
 
 def test_forward_takes_the_ids_products_bitwise():
-    """moe_forward on a batch the grouped path would run in 16-row tiles uses
-    the ids products; its output equals the grouped stages' bit for bit."""
+    """moe_forward on a batch that reaches most experts with under 9 pairs
+    each uses the ids products; its output equals the grouped stages' (16-row
+    tiles) bit for bit."""
     cfg = random_case(48, 256, 64, 8, 128, I_shared=64, seed=47)
     t = make_inputs(cfg, DEV)
     out = moe.moe_forward(t["x"], t["router_w"], t["w_gate_up"], t["w_down"], cfg.top_k, cfg.norm_topk_prob,
