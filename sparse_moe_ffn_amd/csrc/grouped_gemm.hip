@@ -556,6 +556,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
 
 // ---------------------------------------------------------------- float32
 
+constexpr int64_t kOneRound = 256;   // workgroups of one round at one per CU
 constexpr int kF32Cols = 64;
 constexpr int kF32Threads = 256;
 
@@ -643,16 +644,20 @@ hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_
 // g1 (optional, max_tiles 0 for none) must have the same mode, tile height
 // and weight layout as g0; its workgroups follow g0's, from a multiple of 8
 // (the XCD count) so each problem keeps its own XCD-aware tile order.
+// Workgroups of one problem's launch with BN-wide tiles: row tiles times
+// column blocks (a gate/up tile covers BN / 2 gate and as many up columns).
+template <int BN, int MODE>
+static int64_t blocks_of(const GemmProblem& g) {
+  const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
+  return (int64_t)g.max_tiles * n_tiles_n;
+}
+
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = kRot, bool SCAN = false>
 static hipError_t launch_bf16(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s) {
   if (g0.block_m != BM || (g1.max_tiles && g1.block_m != BM)) return hipErrorInvalidValue;
   if (g1.max_tiles && g1.weights_blocked != g0.weights_blocked) return hipErrorInvalidValue;
-  auto blocks_of = [](const GemmProblem& g) {
-    const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + BN / 2 - 1) / (BN / 2) : (g.n_out + BN - 1) / BN;
-    return (int64_t)g.max_tiles * n_tiles_n;
-  };
-  int64_t blocks0 = blocks_of(g0);
-  const int64_t blocks1 = g1.max_tiles ? blocks_of(g1) : 0;
+  int64_t blocks0 = blocks_of<BN, MODE>(g0);
+  const int64_t blocks1 = g1.max_tiles ? blocks_of<BN, MODE>(g1) : 0;
   if (blocks1) blocks0 = (blocks0 + 7) / 8 * 8;
   const int64_t blocks = blocks0 + blocks1;
   if (blocks == 0) return hipSuccess;
@@ -711,16 +716,46 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
   // workgroups.  A dense down launch at 16 and 32 rows takes 64-column
   // tiles (twice the workgroups over its long K): dense layer (H=2048,
   // I=6144) at 16 / 32 / 64 tokens 52.0 / 53.2 / 54.3 us against 58.5 /
-  // 56.4 / 55.3 with 128 columns.
+  // 56.4 / 55.3 with 128 columns.  While such a launch has at most one
+  // workgroup per CU, each workgroup's 96 K stages are bound by load
+  // latency, so it keeps three A stages and five weight stages in flight (4
+  // and 6 slots): the same layer at 16 / 64 / 128 / 256 tokens 45.4 / 47.2
+  // / 60.3 / 63.0 us against 52.1 / 54.4 / 68.3 / 73.1 with 2 and 4 slots,
+  // 49.4 / 49.0 / 61.8 / 64.3 with 3 and 6, 49.1 / 48.2 / 61.1 / 63.4 with
+  // 5 and 6.  Only the A ring's depth counts: 2 and 6 slots gave 51.8 /
+  // 55.6 / 68.4 / 73.7.  Past 256 workgroups the deeper rings' LDS (64 KB
+  // against 40 at 32 rows) cuts the workgroups a CU holds from three to two,
+  // and co-resident workgroups hide the latency anyway: at 768 tokens (768
+  // workgroups) 132.0 us against 102.8 with 2 and 4 slots.  Past three
+  // workgroups per CU a 32-row launch takes 128-column tiles (two per CU)
+  // rather than a second round: 896 / 1024 tokens 102.0 / 105.2 us against
+  // 134.6 / 140.3 with 64 columns.  A dense gate/up launch of one round at
+  // 16 and 32 rows keeps three A stages in flight too (4 A and 4 weight
+  // slots): the layer at 16 / 32 / 64 tokens 42.9 / 45.6 / 46.7 us against
+  // 44.7 / 46.3 / 47.3, the talker layer (with the shared expert on dense
+  // tiles) at 32 / 64 / 128 tokens 199.3 / 214.9 / 235.4 us against 200.7 /
+  // 215.8 / 238.4.
   const bool grouped = g.sorted_pairs != nullptr || (g1.max_tiles && g1.sorted_pairs != nullptr);
   switch (g.block_m) {
     case 16:   // small batches; grouped down one weight slot shorter (75 -> 74 us)
-      if constexpr (MODE == kGateUp) return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
-      else if (!grouped) return launch_bf16<16, 64, 64, 1, 4, 2, 4, MODE>(g, g1, s);
-      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE>(g, g1, s);
+      if constexpr (MODE == kGateUp) {
+        if (!grouped && blocks_of<128, MODE>(g) <= kOneRound)
+          return launch_bf16<16, 128, 64, 1, 2, 4, 4, MODE>(g, g1, s);
+        return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
+      } else if (!grouped) {
+        if (blocks_of<64, MODE>(g) <= kOneRound) return launch_bf16<16, 64, 64, 1, 4, 4, 6, MODE>(g, g1, s);
+        return launch_bf16<16, 64, 64, 1, 4, 2, 4, MODE>(g, g1, s);
+      }
+      return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE>(g, g1, s);
     case 32:
       if (grouped) return launch_bf16<32, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);
-      if constexpr (MODE == kDown) return launch_bf16<32, 64, 64, 1, 4, 2, 4, MODE>(g, g1, s);
+      if constexpr (MODE == kDown) {
+        const int64_t b = blocks_of<64, MODE>(g);
+        if (b <= kOneRound) return launch_bf16<32, 64, 64, 1, 4, 4, 6, MODE>(g, g1, s);
+        if (b <= 3 * kOneRound) return launch_bf16<32, 64, 64, 1, 4, 2, 4, MODE>(g, g1, s);
+        return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, g1, s);
+      }
+      if (blocks_of<128, MODE>(g) <= kOneRound) return launch_bf16<32, 128, 64, 1, 4, 4, 4, MODE>(g, g1, s);
       return launch_bf16<32, 128, 64, 1, 4, 2, 4, MODE>(g, g1, s);
     case 64:
       if (grouped) return launch_bf16<64, 256, 64, 2, 4, 2, 3, MODE>(g, g1, s);

@@ -130,30 +130,31 @@ int64_t dense_block_m(const moe_problem* p, int64_t inter) {
 
 // Row-tile height of a dense down product: the tallest height up to the
 // gate/up one whose launch still has 160 workgroups, ceil(N / h) row tiles
-// times the column blocks of H (256 columns from 64 rows up, 64 below),
-// else the shortest of them down to 32 rows.  The down product's K (the
-// intermediate size) is long for dense layers, so a launch with few
-// workgroups keeps most CUs idle throughout.  Measured on the dense SwiGLU
+// times 256-column blocks of H; else 32 rows while the launch of 32x128
+// tiles fits one round (512 workgroups, two per CU; the launcher narrows
+// them to 64 columns while that fits a round too); else 64 rows.  The down
+// product's K (the intermediate size) is long for dense layers, so a launch
+// with few workgroups keeps most CUs idle throughout, and a launch a little
+// past one round pays for a whole second one.  Measured on the dense SwiGLU
 // layer (H=2048, I=6144, blocked weights), whole layer: 256 tokens 32-row
 // down tiles 72.8 us against 99.3 with 64; 512 tokens 32 rows 76.6 against
-// 101.9 with 64; 1024 tokens 32 rows 109.4 against 126.8 with 64; 1280
-// tokens 64 rows 126.0 against 140.5 with 32; 2048 tokens 64 rows 189.0
-// against 201.0 with 128; 2560 tokens 128 rows 204.7 against 252.0 with
-// 64; 4096 tokens 128 rows 278.3 against 321.4 with 64.  16-row tiles were
-// never faster than 32-row ones there, so they are left to 16-row gate/up
-// tiles.  Every tile height sums each element in one K order, so the result
-// does not change.
+// 101.9 with 64; 1024 tokens 32x128 tiles 105.2 against 127.6 with 64 rows
+// and 140.3 with 32x64 (1024 workgroups, three per CU); 1152 tokens 64 rows
+// 126.8 against 137.9 with 32x128 (576 workgroups); 2048 tokens 64 rows
+// 189.0 against 201.0 with 128; 2560 tokens 128 rows 204.7 against 252.0
+// with 64; 4096 tokens 128 rows 278.3 against 321.4 with 64.  16-row tiles
+// were never faster than 32-row ones there, so they are left to 16-row
+// gate/up tiles.  Every tile height sums each element in one K order, so
+// the result does not change.
 int64_t dense_down_block_m(const moe_problem* p, int64_t bm) {
   if (p->dtype == MOE_F32) return bm;
   const int64_t N = p->num_tokens, H = p->hidden;
-  int64_t chosen = bm;
-  for (int64_t h : {320, 128, 64, 32}) {
-    if (h > bm) continue;
-    chosen = h;
-    const int64_t cols = (h >= 64) ? 256 : 64;        // output columns per workgroup
-    if (((N + h - 1) / h) * ((H + cols - 1) / cols) >= 160) break;
-  }
-  return chosen;
+  auto blocks = [&](int64_t h, int64_t cols) { return ((N + h - 1) / h) * ((H + cols - 1) / cols); };
+  for (int64_t h : {320, 128, 64})
+    if (h <= bm && blocks(h, 256) >= 160) return h;
+  if (bm < 32) return bm;
+  if (bm == 32 || blocks(32, 128) <= 512) return 32;
+  return 64;
 }
 
 bool block_m_supported(int32_t dtype, int64_t bm) {

@@ -42,8 +42,9 @@ def check(out, ref, dtype, what):
 
 # The trailing comments give the gate/up row-tile height the library picks
 # (the tallest that still fills half the CUs) and the down height where it
-# differs (the tallest that gives 160 workgroups, else 32 rows).  Every case
-# ends in a ragged row tile.
+# differs (the tallest that gives 160 workgroups, else 32 rows while a launch
+# of 32x128 tiles fits one round, else 64).  Every case ends in a ragged row
+# tile.
 DENSE_SMALL = [(1, 64, 64, "bf16"), (37, 128, 192, "bf16"),            # 16
                (200, 256, 128, "bf16"), (333, 192, 448, "bf16"),       # 16
                (200, 256, 1472, "bf16"), (4100, 128, 64, "bf16"),      # 32
@@ -51,6 +52,8 @@ DENSE_SMALL = [(1, 64, 64, "bf16"), (37, 128, 192, "bf16"),            # 16
                (2500, 1024, 512, "bf16"),                              # 64
                (1300, 1024, 2048, "bf16"),                             # 128 (down 32)
                (700, 128, 5440, "bf16"),                               # 320 (down 32), ragged column block
+               (1000, 2048, 512, "bf16"),                              # 32 (down 32x128: 1024 32x64 tiles)
+               (1100, 2048, 1024, "bf16"),                             # 64 (down 64: 32x128 past a round)
                (5, 24, 40, "f32"), (70, 33, 17, "f32")]
 
 
@@ -66,8 +69,11 @@ def test_dense_mlp_small(N, H, I, dtype):
 @pytest.mark.parametrize("N,H,I", [(2900, 4096, 1664),    # gate/up and down 320-row tiles
                                    (4096, 2048, 6144),    # 320 / 128
                                    (2048, 2048, 6144),    # 320 / 64
+                                   (1152, 2048, 6144),    # 320 / 64 (32x128 tiles past a round)
+                                   (1024, 2048, 6144),    # 320 / 32 with 128 columns
                                    (512, 2048, 6144),     # 128 / 32
-                                   (64, 2048, 6144)])     # 32 / 32
+                                   (64, 2048, 6144),      # 32 / 32
+                                   (16, 2048, 6144)])     # 16 / 16
 def test_dense_tile_heights_bitwise(N, H, I):
     """Rows of a dense layer computed alone (16-row tiles for both products)
     equal the same rows inside the batch, whose tiles are taller, bit for
