@@ -220,7 +220,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
         src_row = min(row0 + r, g.dense_rows - 1);
       }
     } else {
-      src_row = grouped ? (row0 + r) : min(row0 + r, g.dense_rows - 1);
+      // Padding rows of a grouped tile were never written: they read a real
+      // row of the same tile instead (already on its way for another lane),
+      // not HBM.  Their results are dropped.  Fetched per launch (counter
+      // passes): prefill layer 456.2 MB against 468.8, talker 511.3 against
+      // 536.2, skew 924.5 against 955.0; whole forward 213.9 / 228.1 /
+      // 901.2 us against 215.1 / 228.8 / 904.0 at 400 / 640 / 8192 tokens
+      // (talker), prefill unchanged.  Reading the last real row for all of
+      // them instead cost prefill 1-3 us.
+      src_row = grouped ? (row0 + (r < rows_valid ? r : r % max(rows_valid, 1)))
+                        : min(row0 + r, g.dense_rows - 1);
     }
     src_a[q] = A + src_row * K + chunk * 8;
   }
