@@ -407,14 +407,16 @@ def test_staged_calls_equal_forward():
 @pytest.mark.parametrize("N,H,E,k,Is", [(1100, 256, 128, 8, 64), (1200, 128, 64, 4, 0), (1031, 192, 160, 6, 32),
                                         (2048, 2048, 128, 8, 0), (2100, 256, 128, 8, 64),
                                         (4099, 128, 160, 6, 32), (3000, 192, 512, 32, 0),
-                                        (8200, 128, 128, 8, 64), (16400, 64, 128, 8, 64)])
+                                        (8200, 128, 128, 8, 64), (16400, 64, 128, 8, 64),
+                                        (1500, 256, 100, 12, 64)])
 def test_router_tilings_bitwise_equal(N, H, E, k, Is):
     """Batches of 1024 tokens and more compute their logits in 64-token
     tiles (x fragments shared through LDS) placed by XCD, smaller ones in
     one-wave workgroups of 16 tokens and three 16-column sub-tiles;
     a token's ids, weights and shared gate must be bit for bit the same
-    whichever batch routed it (also at the layer's own H = 2048 and at
-    E = 512)."""
+    whichever batch routed it (also at the layer's own H = 2048, at H = 64
+    where most slices are empty, at E = 512, and with k > 8, the
+    radix-select path)."""
     cfg = random_case(N, H, E, k, 64, I_shared=Is, dtype="bf16", seed=3)
     t = make_inputs(cfg, DEV)
     gate = t["shared_gate"]
