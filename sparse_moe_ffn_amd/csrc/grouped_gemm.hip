@@ -772,6 +772,7 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
     case 128:   // 3 A slots (144 KB): 704 / 1024 / 1280 tokens 235.5 / 246.8 / 255.4 us against 236.5 / 249.9 / 257.4
       return launch_bf16<128, 256, 64, 2, 4, 3, 3, MODE>(g, g1, s);
     case 320: return launch_bf16<320, 256, 64, 4, 2, 2, 2, MODE>(g, g1, s);
+    case 256: return launch_bf16<256, 256, 64, 4, 2, 2, 2, MODE>(g, g1, s);   // dense layers
     default: return hipErrorInvalidValue;
   }
 }

@@ -118,12 +118,26 @@ int64_t choose_block_m(const moe_problem* p) {
 // 138.8 with 128; 3072 tokens 320 rows 207.5 against 274.7 with 128.  The
 // talker's shared expert (8192 rows, I_s = 2048) keeps 320-row tiles (416
 // workgroups; 128-row tiles took 218 against 199 us there).
-int64_t dense_block_m(const moe_problem* p, int64_t inter) {
+// A dense layer (dense_layer set) takes 256-row tiles instead of 320-row
+// ones when that is fewer rows per CU over the launch: rounds of 256
+// workgroups (one per CU) times the tile height, ties to 320.  The same
+// layer, whole: 768 / 1024 / 2048 / 2560 / 4096 tokens 98.2 / 97.8 / 179.0
+// / 199.0 / 277.7 us with 256 rows against 103.1 / 105.9 / 193.7 / 209.0 /
+// 285.4 with 320 (the same rounds of shorter tiles); where 256 rows add a
+// round they lose: 1536 / 3072 tokens 172.6 / 250.1 against 135.3 / 221.9.
+// The shared expert keeps 320 rows, the routed products' height, so the two
+// still share their launches.
+int64_t dense_block_m(const moe_problem* p, int64_t inter, bool dense_layer = false) {
   if (p->dtype == MOE_F32) return 16;
   const int64_t N = p->num_tokens;
-  for (int64_t h : {320, 128, 64, 32}) {
+  auto blocks = [&](int64_t h) {
     const int64_t cols = (h >= 64) ? 128 : 64;        // gate (and as many up) columns per workgroup
-    if (((N + h - 1) / h) * ((inter + cols - 1) / cols) >= 128) return h;
+    return ((N + h - 1) / h) * ((inter + cols - 1) / cols);
+  };
+  for (int64_t h : {320, 128, 64, 32}) {
+    if (blocks(h) < 128) continue;
+    if (h == 320 && dense_layer && (blocks(256) + 255) / 256 * 256 < (blocks(320) + 255) / 256 * 320) return 256;
+    return h;
   }
   return 16;
 }
@@ -259,9 +273,9 @@ int check_ptrs_bf16(const moe_problem* p, std::initializer_list<const void*> ptr
 // keeps the gate/up height.
 void dense_problems(const moe_problem* p, int64_t inter, const void* x, const void* w_gate_up, const void* w_down,
                     const float* scale, void* act, void* c, moe::GemmProblem* gu, moe::GemmProblem* dn,
-                    bool fill_down = true) {
+                    bool fill_down = true, bool dense_layer = false) {
   const int64_t N = p->num_tokens;
-  const int64_t bm = dense_block_m(p, inter);
+  const int64_t bm = dense_block_m(p, inter, dense_layer);
   moe::GemmProblem g = gemm_common(p);
   g.dense_rows = (int32_t)N;
   g.block_m = (int32_t)bm;
@@ -288,9 +302,9 @@ void dense_problems(const moe_problem* p, int64_t inter, const void* x, const vo
 
 int dense_swiglu(const moe_problem* p, int64_t inter, const void* x, const void* w_gate_up,
                  const void* w_down, const float* scale, void* act, void* c, hipStream_t stream,
-                 const char* what_gate_up, const char* what_down) {
+                 const char* what_gate_up, const char* what_down, bool dense_layer = false) {
   moe::GemmProblem gu, dn;
-  dense_problems(p, inter, x, w_gate_up, w_down, scale, act, c, &gu, &dn);
+  dense_problems(p, inter, x, w_gate_up, w_down, scale, act, c, &gu, &dn, true, dense_layer);
   if (int rc = hip_status(moe::launch_gate_up(gu, stream), what_gate_up)) return rc;
   return hip_status(moe::launch_down(dn, stream), what_down);
 }
@@ -532,7 +546,7 @@ int moe_dense_mlp(const moe_problem* p, const void* x, const void* w_gate_up, co
   if (!x || !w_gate_up || !w_down || !act || !out) return fail(MOE_EINVAL, "NULL tensor");
   if (int rc = check_ptrs_bf16(p, {x, w_gate_up, w_down, act, out})) return rc;
   return dense_swiglu(p, p->inter, x, w_gate_up, w_down, nullptr, act, out, (hipStream_t)stream,
-                      "dense gate_up", "dense down") ?: ok();
+                      "dense gate_up", "dense down", true) ?: ok();
 }
 
 int moe_add_rmsnorm(int64_t num_tokens, int64_t hidden, int32_t dtype, const void* x, const void* residual_in,

@@ -41,7 +41,8 @@ def check(out, ref, dtype, what):
 # ------------------------------------------------------------ dense SwiGLU
 
 # The trailing comments give the gate/up row-tile height the library picks
-# (the tallest that still fills half the CUs) and the down height where it
+# (the tallest that still fills half the CUs, 256 instead of 320 rows when
+# that takes no more rounds of workgroups) and the down height where it
 # differs (the tallest that gives 160 workgroups, else 32 rows while a launch
 # of 32x128 tiles fits one round, else 64).  Every case ends in a ragged row
 # tile.
@@ -51,7 +52,8 @@ DENSE_SMALL = [(1, 64, 64, "bf16"), (37, 128, 192, "bf16"),            # 16
                (600, 128, 2048, "bf16"), (4200, 256, 320, "bf16"),     # 64 (down 32)
                (2500, 1024, 512, "bf16"),                              # 64
                (1300, 1024, 2048, "bf16"),                             # 128 (down 32)
-               (700, 128, 5440, "bf16"),                               # 320 (down 32), ragged column block
+               (700, 128, 5440, "bf16"),                               # 256 (down 32), ragged column block
+               (1900, 128, 5120, "bf16"),                              # 320 (256 rows: a second round)
                (1000, 2048, 512, "bf16"),                              # 32 (down 32x128: 1024 32x64 tiles)
                (1100, 2048, 1024, "bf16"),                             # 64 (down 64: 32x128 past a round)
                (5, 24, 40, "f32"), (70, 33, 17, "f32")]
@@ -66,11 +68,13 @@ def test_dense_mlp_small(N, H, I, dtype):
     check(host(out), ref, dtype, f"dense N{N} H{H} I{I} {dtype}")
 
 
-@pytest.mark.parametrize("N,H,I", [(2900, 4096, 1664),    # gate/up and down 320-row tiles
-                                   (4096, 2048, 6144),    # 320 / 128
-                                   (2048, 2048, 6144),    # 320 / 64
-                                   (1152, 2048, 6144),    # 320 / 64 (32x128 tiles past a round)
-                                   (1024, 2048, 6144),    # 320 / 32 with 128 columns
+@pytest.mark.parametrize("N,H,I", [(3072, 4096, 6144),    # gate/up and down 320-row tiles
+                                   (2900, 4096, 1664),    # 256 / 128
+                                   (4096, 2048, 6144),    # 256 / 128
+                                   (2048, 2048, 6144),    # 256 / 64
+                                   (1536, 2048, 6144),    # 320 / 64 (256 rows: a second round)
+                                   (1152, 2048, 6144),    # 256 / 64 (32x128 tiles past a round)
+                                   (1024, 2048, 6144),    # 256 / 32 with 128 columns
                                    (512, 2048, 6144),     # 128 / 32
                                    (64, 2048, 6144),      # 32 / 32
                                    (16, 2048, 6144)])     # 16 / 16
