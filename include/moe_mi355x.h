@@ -98,9 +98,13 @@ typedef struct moe_workspace_layout {
                               (no grouping; act rows are pair indices) */
   int64_t shared_block_m;  /* rows per tile of the shared expert's gate/up
                               product (0 without a shared expert) */
-  int64_t shared_merged;   /* 1: moe_forward runs the shared expert's products
-                              in the routed products' launches (grouped bf16
-                              products of the same tile height) */
+  int64_t shared_merged;   /* products that moe_forward runs in one launch with
+                              the shared expert's tiles: bit 0 gate/up, bit 1
+                              down.  bf16, shared and routed tiles of one
+                              height: 3 for grouped products; for the ids
+                              products each one whose routed launch leaves
+                              room for the shared tiles in its last round of
+                              workgroups (0 otherwise) */
   size_t route_scratch, topk_ids, topk_w, shared_scale;
   size_t counts, offsets, order, sorted_pairs, tile_expert, tile_rows, num_tiles, align_scratch;
   size_t act, y, shared_act, shared_y;

@@ -46,6 +46,7 @@
 // one row tile reads alone is streamed with the non-temporal hint.
 //
 // fp32 kernel: plain FMA loops, any shape (used for float32 layers).
+#include <cmath>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -116,7 +117,7 @@ constexpr int kRot = 13;   // K-start stride of every grouped product (see the l
 // experts and the shared expert's dense rows): workgroups below blocks0 take
 // g0, the others g1; each workgroup's arithmetic is that of a launch of its
 // problem alone.
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK, int ROT, bool SCAN>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, bool BLK, int ROT, int SCAN>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kernel(GemmProblem g0, GemmProblem g1,
                                                                                     int blocks0) {
   const bool second = (int)blockIdx.x >= blocks0;
@@ -159,11 +160,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   // Scan mode (16-row tiles only): the current pass's pairs, and the
   // per-wave match counts of the scan.
   static_assert(!SCAN || BM == 16, "scan mode runs 16-row passes");
-  constexpr bool scan = SCAN;
+  // SCAN 1: scan mode; 2: scan mode for the problem with top-k ids, and
+  // a plain dense problem (the shared expert) beside it.
+  const bool scan = SCAN == 1 || (SCAN == 2 && g.topk_ids != nullptr);
   __shared__ int32_t scan_rows[SCAN ? BM : 1];
   __shared__ int32_t scan_count[SCAN ? NW : 1];
 
-  const bool grouped = !SCAN && g.sorted_pairs != nullptr;
+  const bool grouped = SCAN == 0 && g.sorted_pairs != nullptr;
   const int half = BN / 2;
   const int n_tiles_n = (MODE == kGateUp) ? (g.n_out + half - 1) / half : (g.n_out + BN - 1) / BN;
   // Workgroups past the real number of tiles leave at once; the others are
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
   floatx4 acc[TM][TN];
   // One pass over the tile's rows (scan mode: one per BM pairs of the expert).
   for (int c0 = 0, scan_total = 0;; c0 += BM) {
-  if constexpr (SCAN) {
+  if (scan) {
     scan_total = scan_pass(c0);
     if (c0 >= scan_total) {                            // nothing (left) for this expert
       wait_vmcnt<0>();                                 // the weight stages have landed
@@ -554,10 +557,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_kern
           *reinterpret_cast<const uint4*>(so + rl * OUT_LD + j * 8);
     }
   }
-  if constexpr (!SCAN) {
+  if constexpr (SCAN == 0) {
     break;
   } else {
-    if (c0 + BM >= scan_total) break;
+    if (!scan || c0 + BM >= scan_total) break;
     __syncthreads();                                   // the staged output is read; the next pass reuses the LDS
   }
   }  // passes
@@ -641,18 +644,6 @@ hipError_t launch_pack_weights(const void* src, void* dst, int64_t batch, int64_
 
 // ---------------------------------------------------------------- launchers
 
-// ROT: K-start stride, kRot for every tile shape and both weight layouts,
-// so every output element is summed in one order whatever the tile height:
-// a token's output does not depend on the batch it comes in, nor on the
-// weight layout.  Measured with blocked weights: 16-row tiles at 64 tokens,
-// gate/up 116.6 -> 115.2 us and down 60.7 -> 59.9 us from stride 5 to 13
-// (row-major 116.6 -> 117.3 and 63.1 -> 62.2 us); moe_forward with the
-// 32-, 64-, 128- and 320-row tiles (512 to 16384 tokens) within 1.2 us of
-// strides 7 and 5.
-// SCAN: the small-batch products that scan the top-k ids (16-row tiles).
-// g1 (optional, max_tiles 0 for none) must have the same mode, tile height
-// and weight layout as g0; its workgroups follow g0's, from a multiple of 8
-// (the XCD count) so each problem keeps its own XCD-aware tile order.
 // Workgroups of one problem's launch with BN-wide tiles: row tiles times
 // column blocks (a gate/up tile covers BN / 2 gate and as many up columns).
 template <int BN, int MODE>
@@ -661,7 +652,21 @@ static int64_t blocks_of(const GemmProblem& g) {
   return (int64_t)g.max_tiles * n_tiles_n;
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = kRot, bool SCAN = false>
+// ROT: K-start stride, kRot for every tile shape and both weight layouts,
+// so every output element is summed in one order whatever the tile height:
+// a token's output does not depend on the batch it comes in, nor on the
+// weight layout.  Measured with blocked weights: 16-row tiles at 64 tokens,
+// gate/up 116.6 -> 115.2 us and down 60.7 -> 59.9 us from stride 5 to 13
+// (row-major 116.6 -> 117.3 and 63.1 -> 62.2 us); moe_forward with the
+// 32-, 64-, 128- and 320-row tiles (512 to 16384 tokens) within 1.2 us of
+// strides 7 and 5.
+// SCAN: 1 for the small-batch products that scan the top-k ids (16-row
+// tiles); 2 for such a product with a dense problem beside it (either
+// order), a separate instance so that the scan-only kernel keeps its code.
+// g1 (optional, max_tiles 0 for none) must have the same mode, tile height
+// and weight layout as g0; its workgroups follow g0's, from a multiple of 8
+// (the XCD count) so each problem keeps its own XCD-aware tile order.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int SA, int SB, int MODE, int ROT = kRot, int SCAN = 0>
 static hipError_t launch_bf16(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s) {
   if (g0.block_m != BM || (g1.max_tiles && g1.block_m != BM)) return hipErrorInvalidValue;
   if (g1.max_tiles && g1.weights_blocked != g0.weights_blocked) return hipErrorInvalidValue;
@@ -683,19 +688,21 @@ static hipError_t launch_bf16(const GemmProblem& g0, const GemmProblem& g1, hipS
 
 template <int MODE>
 static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipStream_t s) {
-  if (g.topk_ids && !g.sorted_pairs &&
-      (g.dtype != MOE_BF16 || g.block_m != 16 || g.max_tiles != g.num_experts || g.num_pairs < 4 ||
-       g.num_pairs > kScanMaxPairs || g.num_pairs % 4 != 0))
+  const GemmProblem& sp = (g1.max_tiles && g1.topk_ids) ? g1 : g;   // the scan problem, if any
+  if (sp.topk_ids && !sp.sorted_pairs &&
+      (sp.dtype != MOE_BF16 || sp.block_m != 16 || sp.max_tiles != sp.num_experts || sp.num_pairs < 4 ||
+       sp.num_pairs > kScanMaxPairs || sp.num_pairs % 4 != 0))
     return hipErrorInvalidValue;                       // outside what scan mode is built for
-  if (g1.max_tiles && (g.dtype != MOE_BF16 || g1.dtype != MOE_BF16 || g.topk_ids || g1.topk_ids))
-    return hipErrorInvalidValue;                       // pairs of problems: bf16 tiles only
+  if (g1.max_tiles && (g.dtype != MOE_BF16 || g1.dtype != MOE_BF16 || (g.topk_ids && g1.topk_ids) ||
+                       ((g.topk_ids || g1.topk_ids) && (g.sorted_pairs || g1.sorted_pairs))))
+    return hipErrorInvalidValue;                       // pairs: bf16 tiles; a scan problem pairs with a dense one
   if (g.dtype == MOE_F32) {
     const dim3 grid(g.max_tiles, (g.n_out + kF32Cols - 1) / kF32Cols);
     if (grid.x == 0) return hipSuccess;
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<MODE>, grid, dim3(kF32Threads), 0, s, g);
     return hipGetLastError();
   }
-  if (g.topk_ids && !g.sorted_pairs) {
+  if (sp.topk_ids && !sp.sorted_pairs) {
     // Scan mode: one workgroup per (expert, column block) whatever the
     // routing, so the tile width sets the number of workgroup rounds
     // directly.  Measured at 32 / 64 / 128 tokens (H=2048, E=128, top-8,
@@ -711,9 +718,14 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
     //     60.0 with 8 waves.
     // Results are the same bit for bit: the tile width does not change any
     // row's arithmetic.
-    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, kRot, true>(g, g1, s);
-    else if (g.num_pairs <= 4 * g.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, kRot, true>(g, g1, s);
-    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, kRot, true>(g, g1, s);
+    if (g1.max_tiles) {
+      if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, kRot, 2>(g, g1, s);
+      else if (sp.num_pairs <= 4 * sp.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, kRot, 2>(g, g1, s);
+      else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, kRot, 2>(g, g1, s);
+    }
+    if constexpr (MODE == kGateUp) return launch_bf16<16, 256, 64, 1, 4, 2, 3, MODE, kRot, 1>(g, g1, s);
+    else if (sp.num_pairs <= 4 * sp.num_experts) return launch_bf16<16, 256, 64, 1, 4, 2, 2, MODE, kRot, 1>(g, g1, s);
+    else return launch_bf16<16, 128, 64, 1, 2, 2, 3, MODE, kRot, 1>(g, g1, s);
   }
   // Grouped launches (the routed experts, alone or with the shared expert's
   // tiles) take 8 waves at 32 and 64 rows; dense launches keep the shapes
@@ -775,6 +787,37 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
     case 256: return launch_bf16<256, 256, 64, 4, 2, 2, 2, MODE>(g, g1, s);   // dense layers
     default: return hipErrorInvalidValue;
   }
+}
+
+// Expected experts with at least one of P pairs under uniform routing, the
+// routed scan launch's workgroups (one per hit expert and column block), and
+// the idle slots of its last round: the shared expert's tiles join the
+// launch when their work (in routed-workgroup lengths: the K ratio) fits
+// there.  Workgroups per CU follow from the scan configurations above:
+// gate/up 16x256 one per CU, down 16x256 two (at most 4 pairs per expert)
+// or 16x128 three.  Talker layer (H=2048, E=128, top-8, I=768, I_s=2048),
+// whole forward, bit for bit equal: 24 / 32 tokens (both merged) 168.1 /
+// 181.3 us against 189.7 / 199.3 with separate shared launches; 80 / 96
+// tokens (down merged) 209.4 / 213.3 against 217.5 / 220.8; merging a
+// product that the rule keeps apart lost 2-8 us (48 / 64 tokens, gate/up
+// at 80 / 96 tokens).
+int scan_shared_merge(int64_t num_pairs, int64_t num_experts, int64_t num_tokens, int64_t hidden, int64_t inter,
+                      int64_t shared_inter) {
+  const double E = (double)num_experts, P = (double)num_pairs;
+  const double hit = E * (1.0 - std::pow(1.0 - 1.0 / E, P));
+  const double row_tiles = (double)((num_tokens + 15) / 16);
+  auto fits = [](double routed, double per_round, double shared) {
+    return shared <= std::ceil(routed / per_round) * per_round - routed;
+  };
+  auto cdiv = [](int64_t a, int64_t b) { return (double)((a + b - 1) / b); };
+  int mask = 0;
+  if (fits(hit * cdiv(inter, 128), 256, row_tiles * cdiv(shared_inter, 128))) mask |= 1;
+  const bool wide = num_pairs <= 4 * num_experts;
+  const int64_t cols = wide ? 256 : 128;
+  if (fits(hit * cdiv(hidden, cols), wide ? 512 : 768,
+           row_tiles * cdiv(hidden, cols) * (double)shared_inter / (double)inter))
+    mask |= 2;
+  return mask;
 }
 
 static const GemmProblem kNoProblem{};

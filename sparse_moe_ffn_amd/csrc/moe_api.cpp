@@ -211,8 +211,14 @@ void layout_of(const moe_problem* p, moe_workspace_layout* L) {
   L->block_m = L->ids_products ? 16 : choose_block_m(p);   // the ids products run 16-row passes
   capacity(P, E, L->block_m, &L->max_rows, &L->max_tiles);
   L->shared_block_m = p->shared_inter > 0 ? dense_block_m(p, p->shared_inter) : 0;
-  L->shared_merged = (p->shared_inter > 0 && !L->ids_products && p->dtype == MOE_BF16 &&
-                      L->shared_block_m == L->block_m) ? 1 : 0;
+  // Products whose launch also runs the shared expert's tiles (bit 0 gate/up,
+  // bit 1 down): both for grouped tiles of the same height; for the ids
+  // products (16-row tiles) those where the shared tiles fit the last round.
+  L->shared_merged = 0;
+  if (p->shared_inter > 0 && p->dtype == MOE_BF16 && L->shared_block_m == L->block_m)
+    L->shared_merged = L->ids_products ? moe::scan_shared_merge(P, p->num_experts, N, p->hidden, p->inter,
+                                                                p->shared_inter)
+                                       : 3;
   size_t off = 0;
   auto region = [&](size_t bytes) {
     off = (off + 255) & ~(size_t)255;
@@ -256,6 +262,31 @@ moe::GemmProblem ids_problem(const moe_problem* p, const int32_t* topk_ids) {
   g.num_experts = (int32_t)p->num_experts;
   g.block_m = 16;
   g.max_tiles = (int32_t)p->num_experts;
+  return g;
+}
+
+moe::GemmProblem ids_gate_up_problem(const moe_problem* p, const void* x, const void* w_gate_up,
+                                     const int32_t* topk_ids, void* act) {
+  moe::GemmProblem g = ids_problem(p, topk_ids);
+  g.a = x;
+  g.b = w_gate_up;
+  g.c = act;
+  g.expert_stride = 2 * p->inter * p->hidden;
+  g.K = (int32_t)p->hidden;
+  g.n_out = (int32_t)p->inter;
+  return g;
+}
+
+moe::GemmProblem ids_down_problem(const moe_problem* p, const void* act, const void* w_down,
+                                  const int32_t* topk_ids, const float* topk_w, void* y) {
+  moe::GemmProblem g = ids_problem(p, topk_ids);
+  g.a = act;
+  g.b = w_down;
+  g.c = y;
+  g.scale = topk_w;
+  g.expert_stride = p->hidden * p->inter;
+  g.K = (int32_t)p->inter;
+  g.n_out = (int32_t)p->hidden;
   return g;
 }
 
@@ -496,14 +527,8 @@ int moe_gate_up_ids(const moe_problem* p, const void* x, const void* w_gate_up, 
     return fail(MOE_EUNSUPPORTED, "needs bf16 and 4 <= N*k <= %d with N*k a multiple of 4", moe::kScanMaxPairs);
   if (!aligned16(topk_ids)) return fail(MOE_EUNSUPPORTED, "topk_ids must be 16-byte aligned");
   if (int rc = check_ptrs_bf16(p, {x, w_gate_up, act})) return rc;
-  moe::GemmProblem g = ids_problem(p, topk_ids);
-  g.a = x;
-  g.b = w_gate_up;
-  g.c = act;
-  g.expert_stride = 2 * p->inter * p->hidden;
-  g.K = (int32_t)p->hidden;
-  g.n_out = (int32_t)p->inter;
-  return hip_status(moe::launch_gate_up(g, (hipStream_t)stream), "gate_up_ids") ?: ok();
+  return hip_status(moe::launch_gate_up(ids_gate_up_problem(p, x, w_gate_up, topk_ids, act), (hipStream_t)stream),
+                    "gate_up_ids") ?: ok();
 }
 
 int moe_down_ids(const moe_problem* p, const void* act, const void* w_down, const int32_t* topk_ids,
@@ -515,15 +540,8 @@ int moe_down_ids(const moe_problem* p, const void* act, const void* w_down, cons
     return fail(MOE_EUNSUPPORTED, "needs bf16 and 4 <= N*k <= %d with N*k a multiple of 4", moe::kScanMaxPairs);
   if (!aligned16(topk_ids)) return fail(MOE_EUNSUPPORTED, "topk_ids must be 16-byte aligned");
   if (int rc = check_ptrs_bf16(p, {act, w_down, y})) return rc;
-  moe::GemmProblem g = ids_problem(p, topk_ids);
-  g.a = act;
-  g.b = w_down;
-  g.c = y;
-  g.scale = topk_w;
-  g.expert_stride = p->hidden * p->inter;
-  g.K = (int32_t)p->inter;
-  g.n_out = (int32_t)p->hidden;
-  return hip_status(moe::launch_down(g, (hipStream_t)stream), "down_ids") ?: ok();
+  return hip_status(moe::launch_down(ids_down_problem(p, act, w_down, topk_ids, topk_w, y), (hipStream_t)stream),
+                    "down_ids") ?: ok();
 }
 
 int moe_shared_expert(const moe_problem* p, const void* x, const void* shared_w_gate_up,
@@ -606,9 +624,9 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
                 const void* w_gate_up, const void* w_down, const void* shared_w_gate_up,
                 const void* shared_w_down, const void* shared_gate, void* out, char* ws, void* stream) {
   const bool shared = shared_w_gate_up != nullptr;
-  // The shared expert joins the routed products' launches when both run the
-  // same bf16 tile height.
-  const bool merge_shared = shared && L.shared_merged;
+  // Products whose launch also runs the shared expert's tiles (bit 0
+  // gate/up, bit 1 down; see the layout).
+  const int merge = shared ? (int)L.shared_merged : 0;
   auto at = [&](size_t off) { return static_cast<void*>(ws + off); };
   int32_t* ids = (int32_t*)at(L.topk_ids);
   float* w = (float*)at(L.topk_w);
@@ -619,8 +637,33 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
   if (L.ids_products) {
     // Small batch: the products find their expert's pairs themselves (no
     // align launch); act and y rows are pair indices.
-    if (int rc = moe_gate_up_ids(p, x, w_gate_up, ids, at(L.act), stream)) return rc;
-    if (int rc = moe_down_ids(p, at(L.act), w_down, ids, w, at(L.y), stream)) return rc;
+    const moe::GemmProblem gu = ids_gate_up_problem(p, x, w_gate_up, ids, at(L.act));
+    const moe::GemmProblem dn = ids_down_problem(p, at(L.act), w_down, ids, w, at(L.y));
+    if (merge) {
+      // The shared expert's 16-row tiles first, so that its long workgroups
+      // (the down product's K is I_s) start in the first round; a product
+      // that does not merge runs them in a launch of their own after it.
+      moe::GemmProblem sgu, sdn;
+      dense_problems(p, p->shared_inter, x, shared_w_gate_up, shared_w_down, sscale, at(L.shared_act),
+                     at(L.shared_y), &sgu, &sdn, /*fill_down=*/(merge & 2) == 0);
+      if (merge & 1) {
+        if (int rc = hip_status(moe::launch_gate_up_pair(sgu, gu, (hipStream_t)stream), "gate_up_ids with shared"))
+          return rc;
+      } else {
+        if (int rc = hip_status(moe::launch_gate_up(gu, (hipStream_t)stream), "gate_up_ids")) return rc;
+        if (int rc = hip_status(moe::launch_gate_up(sgu, (hipStream_t)stream), "shared gate_up")) return rc;
+      }
+      if (merge & 2) {
+        if (int rc = hip_status(moe::launch_down_pair(sdn, dn, (hipStream_t)stream), "down_ids with shared"))
+          return rc;
+      } else {
+        if (int rc = hip_status(moe::launch_down(dn, (hipStream_t)stream), "down_ids")) return rc;
+        if (int rc = hip_status(moe::launch_down(sdn, (hipStream_t)stream), "shared down")) return rc;
+      }
+    } else {
+      if (int rc = hip_status(moe::launch_gate_up(gu, (hipStream_t)stream), "gate_up_ids")) return rc;
+      if (int rc = hip_status(moe::launch_down(dn, (hipStream_t)stream), "down_ids")) return rc;
+    }
   } else {
     int32_t* sorted = (int32_t*)at(L.sorted_pairs);
     int32_t* texp = (int32_t*)at(L.tile_expert);
@@ -630,7 +673,7 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
                            (int32_t*)at(L.offsets), (int32_t*)at(L.order), sorted, texp, trows, ntiles,
                            (int32_t*)at(L.align_scratch), stream))
       return rc;
-    if (merge_shared) {
+    if (merge) {
       // One gate/up and one down launch cover the routed tiles and the shared
       // expert's dense tiles (same tile height): one ramp-up and one tail per
       // product instead of two, and the small shared launches no longer run
@@ -658,7 +701,7 @@ int run_forward(const moe_problem* p, const moe_workspace_layout& L, const void*
         return rc;
     }
   }
-  if (shared && !merge_shared) {
+  if (shared && !merge) {
     if (int rc = moe_shared_expert(p, x, shared_w_gate_up, shared_w_down, sscale, at(L.shared_act),
                                    at(L.shared_y), stream))
       return rc;

@@ -59,10 +59,17 @@ constexpr int kScanMaxPairs = 1024;   // ids that fit the 16-row tile's A ring (
 
 hipError_t launch_gate_up(const GemmProblem& g, hipStream_t s);
 hipError_t launch_down(const GemmProblem& g, hipStream_t s);
-// Two problems in one launch (bf16, same tile height and weight layout, no
-// scan mode): the routed experts' tiles, then the shared expert's dense rows.
+// Two problems in one launch (bf16, same tile height and weight layout): the
+// routed experts' tiles (grouped, or in scan mode with 16-row tiles) and the
+// shared expert's dense rows, in either order.
 hipError_t launch_gate_up_pair(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s);
 hipError_t launch_down_pair(const GemmProblem& g0, const GemmProblem& g1, hipStream_t s);
+// Which scan-mode products take the shared expert's 16-row dense tiles into
+// their launch: bit 0 gate/up, bit 1 down.  A product merges when the
+// shared tiles' work fits the idle slots of the routed launch's last round
+// of workgroups (pairs P over E experts, shared intermediate size I_s).
+int scan_shared_merge(int64_t num_pairs, int64_t num_experts, int64_t num_tokens, int64_t hidden, int64_t inter,
+                      int64_t shared_inter);
 
 // Row-major bf16 [batch, rows, cols] -> the blocked layout (rows % 8 == 0,
 // cols % 64 == 0).

@@ -405,13 +405,19 @@ def test_route_rejects_misaligned_scratch_before_any_hip_call():
 
 
 def test_shared_expert_tile_height_and_merge():
-    """The layout reports the shared expert's tile height and whether
-    moe_forward runs its products in the routed launches (host arithmetic)."""
+    """The layout reports the shared expert's tile height and which products
+    moe_forward runs in one launch with the routed tiles (bit 0 gate/up,
+    bit 1 down; host arithmetic)."""
     L = lambda *a, **kw: moe.moe_get_workspace_layout(moe.problem(*a, **kw))
     talker = L(8192, 2048, 128, 8, 768, 2048)          # routed 320, shared 320
-    assert (talker["block_m"], talker["shared_block_m"], talker["shared_merged"]) == (320, 320, 1)
-    small = L(64, 2048, 128, 8, 768, 2048)             # the ids products: never merged
-    assert small["ids_products"] == 1 and small["shared_merged"] == 0 and small["shared_block_m"] == 16
+    assert (talker["block_m"], talker["shared_block_m"], talker["shared_merged"]) == (320, 320, 3)
+    # The ids products take the shared tiles where they fit the last round of
+    # the routed launch: expected hit experts E (1 - (1 - 1/E)^P) times the
+    # column blocks, rounds of 256 (gate/up) or 512 / 768 (down) workgroups.
+    for N, bits in ((24, 3), (32, 3), (48, 0), (64, 0), (80, 2), (96, 2)):
+        small = L(N, 2048, 128, 8, 768, 2048)
+        assert (small["ids_products"], small["shared_block_m"], small["shared_merged"]) == (1, 16, bits), N
+    assert L(53, 960, 92, 8, 64, 128)["shared_merged"] == 1
     plain = L(4096, 2048, 128, 8, 768)                 # no shared expert
     assert (plain["shared_block_m"], plain["shared_merged"]) == (0, 0)
     apart = L(700, 192, 300, 8, 64, 192)               # routed 64, shared 16

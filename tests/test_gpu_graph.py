@@ -1,6 +1,7 @@
 """moe_forward and moe_forward_noalloc captured in a HIP graph on the grouped
 paths (align in several chunks, 64- and 320-row tiles, the shared expert in
-the same launches as the routed experts): each graph is captured once and
+the same launches as the routed experts) and on the ids products with the
+shared expert partly merged: each graph is captured once and
 replayed on new inputs, with the program's own eager work and
 synchronisations between the replays, and every replay must equal the eager
 call bit for bit.  (The decode path, which skips the grouping, is replayed
@@ -26,10 +27,12 @@ CASES = [
     # N, H, E, k, I, I_shared, shared expert in the routed launches:
     # N*k > 4096 pairs (several align chunks), 128-row tiles
     (1000, 256, 72, 8, 128, 0, 0),
-    # 320-row tiles, shared expert in the routed launches
-    (4200, 256, 16, 2, 128, 1280, 1),
+    # 320-row tiles, shared expert in the routed launches (both products)
+    (4200, 256, 16, 2, 128, 1280, 3),
     # one align workgroup, 64-row tiles, shared expert in 16-row launches of its own
     (300, 192, 32, 4, 64, 128, 0),
+    # the ids products (no grouping), shared tiles in the routed down launch only
+    (80, 2048, 128, 8, 768, 2048, 2),
 ]
 
 

@@ -460,18 +460,23 @@ def test_forward_multichunk_grouping_equals_staged(N, H, E, k, I, Is):
 
 
 @pytest.mark.parametrize("N,H,E,k,I,Is,height,merged", [
-    (4100, 128, 8, 2, 64, 1280, 320, 1),      # routed and shared tiles both 320 rows: one launch per product
-    (1000, 128, 80, 8, 64, 2048, 128, 1),
-    (600, 128, 128, 8, 64, 1664, 64, 1),
-    (200, 128, 128, 8, 64, 1216, 32, 1),
-    (20, 128, 128, 8, 64, 128, 16, 1),        # grouped 16-row tiles (too few pairs for the ids products)
+    (4100, 128, 8, 2, 64, 1280, 320, 3),      # routed and shared tiles both 320 rows: one launch per product
+    (1000, 128, 80, 8, 64, 2048, 128, 3),
+    (600, 128, 128, 8, 64, 1664, 64, 3),
+    (200, 128, 128, 8, 64, 1216, 32, 3),
+    (20, 128, 128, 8, 64, 128, 16, 3),        # grouped 16-row tiles (too few pairs for the ids products)
     (700, 192, 300, 8, 64, 192, 16, 0),       # routed 64, shared 16: launches of its own
+    (24, 2048, 128, 8, 768, 2048, 16, 3),     # ids products, both take the shared tiles
+    (80, 2048, 128, 8, 768, 2048, 16, 2),     # ids products, down only
+    (53, 960, 92, 8, 64, 128, 16, 1),         # ids products, gate/up only
+    (64, 2048, 128, 8, 768, 2048, 16, 0),     # ids products, shared launches of its own
 ])
 def test_forward_with_shared_equals_staged(N, H, E, k, I, Is, height, merged):
     """moe_forward runs the shared expert's products in the routed products'
-    launches when both take the same tile height (every case here but the
-    last, one per height); the output must equal the staged public calls,
-    whose shared expert runs its own tile heights, bit for bit."""
+    launches (bit 0 gate/up, bit 1 down) when both take the same tile height
+    and, for the ids products, the shared tiles fit the last round of the
+    routed launch; the output must equal the staged public calls, whose
+    shared expert runs its own tile heights, bit for bit."""
     cfg = random_case(N, H, E, k, I, I_shared=Is, dtype="bf16", seed=23)
     t = make_inputs(cfg, DEV)
     for layout in (moe.MOE_LAYOUT_ROW_MAJOR, moe.MOE_LAYOUT_BLOCKED):
