@@ -755,11 +755,17 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
   // slots): the layer at 16 / 32 / 64 tokens 42.9 / 45.6 / 46.7 us against
   // 44.7 / 46.3 / 47.3, the talker layer (with the shared expert on dense
   // tiles) at 32 / 64 / 128 tokens 199.3 / 214.9 / 235.4 us against 200.7 /
-  // 215.8 / 238.4.
+  // 215.8 / 238.4.  A 16-row dense gate/up launch whose 64-column tiles
+  // still fit one round takes them (twice the workgroups): the layer at 8 /
+  // 16 tokens 38.2 / 38.8 us against 41.2 / 41.8, the talker layer at 48 /
+  // 64 tokens (shared expert in launches of its own) 207.4 / 212.6 against
+  // 211.3 / 215.1; at 32 rows they brought nothing.
   const bool grouped = g.sorted_pairs != nullptr || (g1.max_tiles && g1.sorted_pairs != nullptr);
   switch (g.block_m) {
     case 16:   // small batches; grouped down one weight slot shorter (75 -> 74 us)
       if constexpr (MODE == kGateUp) {
+        if (!grouped && blocks_of<64, MODE>(g) <= kOneRound)     // 32 gate + 32 up columns per workgroup
+          return launch_bf16<16, 64, 64, 1, 2, 4, 4, MODE>(g, g1, s);
         if (!grouped && blocks_of<128, MODE>(g) <= kOneRound)
           return launch_bf16<16, 128, 64, 1, 2, 4, 4, MODE>(g, g1, s);
         return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
