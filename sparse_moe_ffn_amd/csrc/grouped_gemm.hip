@@ -759,7 +759,10 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
   // still fit one round takes them (twice the workgroups): the layer at 8 /
   // 16 tokens 38.2 / 38.8 us against 41.2 / 41.8, the talker layer at 48 /
   // 64 tokens (shared expert in launches of its own) 207.4 / 212.6 against
-  // 211.3 / 215.1; at 32 rows they brought nothing.
+  // 211.3 / 215.1; at 32 rows they brought nothing.  A 16-row dense down
+  // launch likewise takes 32-column tiles (2 waves) while they fit one
+  // round: the layer at 1 / 8 / 16 / 24 tokens 35.5 / 35.9 / 36.7 / 42.2 us
+  // against 38.3 / 38.7 / 39.0 / 45.1 with 64 columns.
   const bool grouped = g.sorted_pairs != nullptr || (g1.max_tiles && g1.sorted_pairs != nullptr);
   switch (g.block_m) {
     case 16:   // small batches; grouped down one weight slot shorter (75 -> 74 us)
@@ -770,6 +773,7 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
           return launch_bf16<16, 128, 64, 1, 2, 4, 4, MODE>(g, g1, s);
         return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
       } else if (!grouped) {
+        if (blocks_of<32, MODE>(g) <= kOneRound) return launch_bf16<16, 32, 64, 1, 2, 4, 6, MODE>(g, g1, s);
         if (blocks_of<64, MODE>(g) <= kOneRound) return launch_bf16<16, 64, 64, 1, 4, 4, 6, MODE>(g, g1, s);
         return launch_bf16<16, 64, 64, 1, 4, 2, 4, MODE>(g, g1, s);
       }
