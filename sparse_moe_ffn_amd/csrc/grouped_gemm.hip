@@ -771,6 +771,10 @@ static hipError_t launch_mode(const GemmProblem& g, const GemmProblem& g1, hipSt
           return launch_bf16<16, 64, 64, 1, 2, 4, 4, MODE>(g, g1, s);
         if (!grouped && blocks_of<128, MODE>(g) <= kOneRound)
           return launch_bf16<16, 128, 64, 1, 2, 4, 4, MODE>(g, g1, s);
+        // Grouped, at most one round with 64-column tiles (a single token:
+        // 8 experts x 24 blocks): 38.8 against 40.4 us for the whole forward.
+        if (grouped && blocks_of<64, MODE>(g) + (g1.max_tiles ? blocks_of<64, MODE>(g1) : 0) <= kOneRound)
+          return launch_bf16<16, 64, 64, 1, 2, 2, 4, MODE>(g, g1, s);
         return launch_bf16<16, 128, 64, 1, 2, 2, 4, MODE>(g, g1, s);
       } else if (!grouped) {
         if (blocks_of<32, MODE>(g) <= kOneRound) return launch_bf16<16, 32, 64, 1, 2, 4, 6, MODE>(g, g1, s);
